@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of one routed-expert MoE layer decode on one MI355X.
+
+Workload (headline): one MoE layer, 256 experts with MXFP4 gate/up
+[2048 x 4096] and down [4096 x 2048], fp32 router [256 x 4096], top-6 with
+softmax, one bf16 token (B=1).  The same layer at B=8 (independent tokens,
+tokens grouped per expert) is measured alongside.  Weights are seeded
+synthetic bytes resident in HBM; every step uses a fresh token and the steps
+rotate over several layer instances so repeated reads cannot be served by the
+256 MB last-level cache.
+
+Reported value: effective weight GB/s = algorithmic bytes per step (the
+active experts' three projections read once, plus the router) / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+E, D, F, TOPK = 256, 4096, 2048, 6
+MX_MAT = F * (D // 32) * 17          # 4,456,448 bytes per projection
+ROUTER = E * D * 4                   # 4,194,304 bytes
+HBM_PEAK_GBS = 8000.0
+METRIC = "effective weight GB/s (% of HBM peak) + tokens/s, MoE layer decode B=1 and B=8"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def build_layers(n_layers: int, seed: int):
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    import synth
+    stream = torch.cuda.current_stream().cuda_stream
+    layers = []
+    for l in range(n_layers):
+        mats = []
+        for proj in (synth.PROJ_GATE, synth.PROJ_UP, synth.PROJ_DOWN):
+            buf = torch.empty(E * MX_MAT, dtype=torch.uint8, device="cuda")
+            synth.gpu_fill("mxfp4", buf.data_ptr(), seed, l, 0, E, proj, F * D // 32, stream)
+            mats.append(buf)
+        router = torch.from_numpy(synth.router_weights(seed, l, E, D)).to("cuda")
+        desc = moe.make_layer_desc("mxfp4", router, mats[0], mats[1], mats[2], E, D, F, TOPK,
+                                   MX_MAT, MX_MAT, MX_MAT)
+        layers.append((desc, mats, router))
+    torch.cuda.synchronize()
+    return layers
+
+
+def time_layer(layers, xs, B, steps, warmup, ws, idx_log=None):
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    y = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    nl = len(layers)
+    for i in range(warmup):
+        moe.moe_layer_decode(layers[i % nl][0], xs[i], y, ws)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        j = warmup + i
+        moe.moe_layer_decode(layers[j % nl][0], xs[j], y, ws, idx_log[i] if idx_log is not None else None)
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    return start.elapsed_time(end) / steps, t_wall / steps * 1e3
+
+
+def profile_phases(layers, xs, B, steps, warmup, ws):
+    """Per-kernel durations from hipEvents recorded around each launch."""
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    y = torch.empty((B, D), dtype=torch.float32, device="cuda")
+    nl = len(layers)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for row in evs:
+        for e in row:
+            e.record()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        j = warmup + i
+        moe.moe_layer_decode_profiled(layers[j % nl][0], xs[j], y, ws, [e.cuda_event for e in evs[i]])
+    torch.cuda.synchronize()
+    names = ["route", "gate_up", "down", "combine"]
+    out = {n: float(np.mean([evs[i][p].elapsed_time(evs[i][p + 1]) for i in range(steps)])) for p, n in
+           enumerate(names)}
+    return out
+
+
+def cpu_baseline(seed: int, n_tokens: int):
+    """The oracle on the host cores: B=1 layer decode for a few tokens."""
+    import oracle
+    import synth
+    wr = synth.router_weights(seed, 0, E, D)
+    cache = {}
+
+    def get(e):
+        if e not in cache:
+            cache[e] = tuple(synth.expert_tensor("mxfp4", seed, 0, e, p, n, k)
+                             for p, (n, k) in ((0, (F, D)), (1, (F, D)), (2, (D, F))))
+        return cache[e]
+
+    xs = [synth.token_bf16(900000 + i, 1, D) for i in range(n_tokens)]
+    for x in xs:  # draw the active experts' bytes before timing (input generation)
+        idx, _, _ = oracle.route_topk(wr, x, TOPK)
+        for e in idx[0]:
+            get(int(e))
+    t = time.perf_counter()
+    for x in xs:
+        oracle.layer_decode("mxfp4", get, wr, x, TOPK, F)
+    dt = (time.perf_counter() - t) / n_tokens
+    bytes_step = TOPK * 3 * MX_MAT + ROUTER
+    return {"value": round(bytes_step / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.default_threads(),
+            "kind": "oracle",
+            "sample": f"{n_tokens} B=1 tokens through one 256-expert MXFP4 layer (fp64 oracle, "
+                      f"{dt:.2f} s per token; expert bytes drawn before timing)",
+            "seconds_per_token_layer": round(dt, 4)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--layers", type=int, default=8, help="layer instances the steps rotate over")
+    ap.add_argument("--seed", type=int, default=0x5EED + 1)
+    ap.add_argument("--cpu-tokens", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this decode path "
+              f"runs on a single MI355X; there is no multi-GPU leg).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    import synth
+    torch.cuda.set_device(0)
+    moe.moe_device_check()
+    log(f"building {args.layers} MXFP4 layers ({args.layers * 3 * E * MX_MAT / 1e9:.1f} GB) ...")
+    layers = build_layers(args.layers, args.seed)
+    n_tok = args.warmup + args.steps
+    x1 = [torch.from_numpy(synth.token_bf16(10000 + i, 1, D).view(np.int16)).to("cuda") for i in range(n_tok)]
+    x8 = [torch.from_numpy(synth.token_bf16(20000 + i, 8, D).view(np.int16)).to("cuda") for i in range(n_tok)]
+    ws = torch.empty(moe.moe_layer_workspace_bytes(8, D, F, E, TOPK), dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws)
+
+    log("timing B=1 ...")
+    ms1, wall1 = time_layer(layers, x1, 1, args.steps, args.warmup, ws)
+    log("timing B=8 ...")
+    idx_log = torch.empty((args.steps, 8, TOPK), dtype=torch.int32, device="cuda")
+    ms8, wall8 = time_layer(layers, x8, 8, args.steps, args.warmup, ws, idx_log)
+    uniq = [len(np.unique(r)) for r in idx_log.cpu().numpy()]
+    U8 = float(np.mean(uniq))
+    bytes1 = TOPK * 3 * MX_MAT + ROUTER
+    bytes8 = U8 * 3 * MX_MAT + ROUTER
+    gbs1 = bytes1 / (ms1 * 1e-3) / 1e9
+    gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
+
+    log("per-kernel event timing ...")
+    ph1 = profile_phases(layers, x1, 1, min(args.steps, 100), args.warmup, ws)
+    ph8 = profile_phases(layers, x8, 8, min(args.steps, 100), args.warmup, ws)
+    gu_bytes1 = TOPK * 2 * MX_MAT
+    achieved = gu_bytes1 / (ph1["gate_up"] * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs1, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms1, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": "moe_layer_decode_mxfp4_b1", "experts": E, "top_k": TOPK, "d_model": D,
+                   "d_ff": F, "tokens_per_step": 1, "weight_format": "mxfp4",
+                   "layer_instances_rotated": args.layers},
+        "pct_hbm_peak": round(100 * gbs1 / HBM_PEAK_GBS, 2),
+        "tokens_per_s_layer": round(1e3 / ms1, 1),
+        "bytes_per_step": bytes1,
+        "host_wall_ms_per_step": round(wall1, 5),
+        "b8": {"value": round(gbs8, 2), "unit": "GB/s", "ms_per_step": round(ms8, 5),
+               "pct_hbm_peak": round(100 * gbs8 / HBM_PEAK_GBS, 2),
+               "tokens_per_s_layer": round(8e3 / ms8, 1), "mean_unique_experts": round(U8, 2),
+               "bytes_per_step": round(bytes8)},
+        "kernel_ms": {"b1": {k: round(v, 5) for k, v in ph1.items()},
+                      "b8": {k: round(v, 5) for k, v in ph8.items()}},
+        "roofline": {"kernel": "gate_up (B=1)", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "bytes_per_launch": gu_bytes1},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * moe_decode.h -- C ABI of libmoedecode.so: the routed-expert matvec of
+ * DeepSeek-V4-Flash-style MoE decode on AMD Instinct MI355X (gfx950).
+ *
+ * Every entry point takes plain pointers and sizes.  Unless stated otherwise:
+ *
+ *  - Pointers are DEVICE addresses of caller-owned memory (any allocator:
+ *    hipMalloc, a torch tensor's data_ptr, ...).  The library never
+ *    allocates, frees or retains them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    All work is enqueued on it; results are valid once the stream has
+ *    reached that point.  No entry point synchronises the host.
+ *  - The return value is a moe_status.  Argument errors are detected on the
+ *    host before anything is enqueued (MOE_ERR_ARG / _SHAPE / _WORKSPACE /
+ *    _ALIGN); MOE_ERR_ARCH if the current device is not gfx950; MOE_ERR_HIP
+ *    if a launch is rejected (moe_last_hip_error() then gives the code).
+ *    Nothing is thrown across the ABI.
+ *  - Calls on different streams must not share output or workspace buffers.
+ *
+ * Weight formats (byte layouts as the pages define them):
+ *  MXFP4   17-byte blocks of 32 weights: byte 0 = E8M0 exponent e (scale
+ *          2^(e-127)), bytes 1..16 = 32 E2M1 codes, element 2j in the high
+ *          nibble of byte 1+j and element 2j+1 in the low nibble.
+ *          [ds4.c study notes, glossary "quantization", section "MXFP4";
+ *          nibble order as dequant_fp4 in the DeepSeek-V4-Flash-0731-W4A16
+ *          model card's conversion script.]
+ *  Q2_K    84-byte blocks of 256 weights: scales[16] at 0 (low nibble scale,
+ *          high nibble min, one byte per 16 weights), qs[64] at 16 (2-bit
+ *          codes, weight i in bits 2(i%4) of byte i/4), binary16 d at 80 and
+ *          dmin at 82; w = d*sc*q - dmin*m.  [ds4.c study notes, glossary
+ *          "quantization", section "core principle".]
+ *  INT4G32 codes int32 [N][K/8], weight 8j+i of a row in bits 4i..4i+3 of
+ *          word j, two's complement -8..7; scales bfloat16 [N][K/32];
+ *          w = q * scale.  [DeepSeek-V4-Flash-0731-W4A16 model card,
+ *          "quantization scheme": INT4, group 32, symmetric, BF16 scale.]
+ *  A matrix W[N][K] is N rows of K weights, row-major, rows contiguous.
+ */
+#ifndef MOE_DECODE_H
+#define MOE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,       /* null pointer, negative or zero size where one is required */
+  MOE_ERR_SHAPE = 2,     /* K not a multiple of the block length, B or top_k out of range */
+  MOE_ERR_ARCH = 3,      /* the current HIP device is not gfx950 */
+  MOE_ERR_HIP = 4,       /* a HIP call or kernel launch failed */
+  MOE_ERR_WORKSPACE = 5, /* workspace missing, too small or not 256-byte aligned */
+  MOE_ERR_ALIGN = 6      /* a weight pointer or stride is not suitably aligned */
+};
+
+enum moe_format { MOE_FMT_MXFP4 = 0, MOE_FMT_Q2K = 1, MOE_FMT_INT4G32 = 2 };
+
+#define MOE_MAX_TOKENS 8   /* B: one token plus up to 7 speculative drafts */
+#define MOE_MAX_TOPK 8
+#define MOE_MAX_EXPERTS 256
+
+int moe_abi_version(void);
+const char* moe_status_string(int status);
+/* The hipError_t of the last MOE_ERR_HIP returned on this thread. */
+int moe_last_hip_error(void);
+/* MOE_OK if the current device is gfx950, else MOE_ERR_ARCH (or _HIP). */
+int moe_device_check(void);
+
+/* ------------------------------------------------------------------ matvec
+ * y[b][n] = sum_k W[n][k] * x[b][k] for b < B, with the weights decoded
+ * inside the kernel and fp32 accumulation.  x fp32 [B][K], y fp32 [B][N]
+ * (overwritten).  1 <= B <= MOE_MAX_TOKENS; every token reuses one read of W.
+ * Alignment: MXFP4 and Q2_K blocks 4-byte aligned, INT4 codes 16-byte
+ * aligned, x 16-byte aligned.
+ * Source: the per-block decode of the formats above; the matvec against the
+ * activation is the scalar reference dot of the ds4 notes ("MXFP4"), and
+ * decode is bound by streaming these weights ("Mixed-precision compression
+ * of DeepSeek-V4-Flash", "What compression does not solve").
+ */
+int moe_expert_gemv_mxfp4(const uint8_t* blocks /* [N][K/32][17] */, int N, int K,
+                          const float* x, int B, float* y, void* stream);
+int moe_expert_gemv_q2k(const uint8_t* blocks /* [N][K/256][84] */, int N, int K,
+                        const float* x, int B, float* y, void* stream);
+int moe_expert_gemv_int4g32(const int32_t* q /* [N][K/8] */, const uint16_t* scale_bf16 /* [N][K/32] */,
+                            int N, int K, const float* x, int B, float* y, void* stream);
+
+/* ------------------------------------------------------------------ routing
+ * logits[b][e] = sum_k router_w[e][k] * x[b][k] accumulated in fp64; each
+ * token keeps its top_k experts by logit (larger first, equal logits by
+ * lower index) and gate weights softmax(selected logits).  The pages keep
+ * the top 6 of 256 routed experts ("Mixed-precision compression of
+ * DeepSeek-V4-Flash", "The recipe"); the softmax over the selected logits is
+ * the reading used for the scoring function they leave open.
+ *   router_w fp32 [E][D] (E <= 256), x bfloat16 bits [B][D], 1 <= B <= 8,
+ *   1 <= top_k <= min(8, E).  Outputs: idx int32 [B][top_k] in rank order,
+ *   gate_w fp32 [B][top_k]; logits_out fp64 [B][E] if not NULL.
+ *   ws: >= moe_route_workspace_bytes(B, D, E, top_k) bytes, 256-byte
+ *   aligned, prepared once with moe_workspace_init (the kernels leave it
+ *   reusable).  Alignment: router_w 16 bytes, x_bf16 8 bytes.
+ */
+size_t moe_route_workspace_bytes(int B, int D, int E, int top_k);
+int moe_route_topk(const float* router_w, int E, int D, const uint16_t* x_bf16, int B, int top_k,
+                   int32_t* idx, float* gate_w, double* logits_out, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* ------------------------------------------------------------------ one MoE layer
+ * For each token b: route (as moe_route_topk), then for every selected
+ * expert e in rank order j: g = Wg_e x, u = Wu_e x, h = SiLU(g) * u (fp32,
+ * SiLU(z) = z / (1 + e^-z)), yp_j = Wd_e h, and y[b] = sum_j gate_w[b][j] *
+ * yp_j summed in rank order.  Tokens that pick the same expert share one read
+ * of its weights ("commit more than one token per sweep of the target
+ * weights": "Mixed-precision compression of DeepSeek-V4-Flash", "What
+ * compression does not solve"; the width-(1+K) verify forward, "Width
+ * drift").  gate/up/down are the routed experts' w1/w3/w2 projections named
+ * in the W4A16 model card's quantization scheme.
+ */
+typedef struct moe_layer_desc {
+  int format;        /* enum moe_format, all three projections */
+  int n_experts;     /* E <= 256 */
+  int d_model;       /* D: multiple of 256 for Q2_K, of 32 otherwise */
+  int d_ff;          /* F: same constraint */
+  int top_k;         /* <= 8 */
+  const float* router_w; /* fp32 [E][D] */
+  /* Expert e's projection starts at base + e * stride (bytes).  gate and up
+   * are [F][D], down is [D][F], each in `format`.  For INT4G32 these are the
+   * int32 code arrays and *_scale the bfloat16 scale arrays. */
+  const void* gate;
+  const void* up;
+  const void* down;
+  int64_t gate_stride, up_stride, down_stride;
+  const uint16_t* gate_scale;
+  const uint16_t* up_scale;
+  const uint16_t* down_scale;
+  int64_t gate_scale_stride, up_scale_stride, down_scale_stride;
+} moe_layer_desc;
+
+/* Workspace for moe_layer_decode with up to B tokens (256-byte aligned). */
+size_t moe_layer_workspace_bytes(int B, int D, int F, int E, int top_k);
+/* Prepare a fresh workspace (zeroes its counters); enqueued on `stream`. */
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+/* x bfloat16 bits [B][D]; y fp32 [B][D] (overwritten).  idx_out int32
+ * [B][top_k] and gw_out fp32 [B][top_k] receive the routing if not NULL. */
+int moe_layer_decode(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
+                     size_t ws_bytes, int32_t* idx_out, float* gw_out, void* stream);
+/* Same, recording 5 hipEvent_t (passed as void*) on `stream`: before
+ * routing, after routing, after gate/up, after down, after the combine.
+ * For per-kernel timing only; events may be NULL to skip a record. */
+int moe_layer_decode_profiled(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
+                              void* ws, size_t ws_bytes, int32_t* idx_out, float* gw_out,
+                              void* const* events, void* stream);
+
+/* ------------------------------------------------------------------ layer stack
+ * Residual stream through n_layers MoE layers: for l = 0..n_layers-1,
+ *   x_l = bf16_rne(h_l / sqrt(mean(h_l^2) + eps)),   h_{l+1} = h_l + moe_l(x_l),
+ * with h_0 = h_in (fp32 [B][D]); the result goes to h_out (fp32 [B][D],
+ * may alias h_in).  Attention is outside this path.  The norm is an
+ * unweighted RMSNorm: the pages keep norms in F32 ("The recipe") without
+ * defining them.  eps: 1e-6 in the stacked-layer workload.
+ * ws: >= moe_stack_workspace_bytes(B, D, F, E, top_k). */
+size_t moe_stack_workspace_bytes(int B, int D, int F, int E, int top_k);
+int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* h_in, int B,
+                     float* h_out, double eps, void* ws, size_t ws_bytes, void* stream);
+/* The norm step alone: x_out bfloat16 bits [B][D] from h fp32 [B][D]. */
+int moe_rmsnorm_bf16(const float* h, int B, int D, double eps, uint16_t* x_out, void* stream);
+
+/* ------------------------------------------------------------------ FP4 -> INT4 g32
+ * Per 32-weight group (= one MXFP4 block of a row): w_i = E2M1[c_i] *
+ * 2^(e-127) in fp32; amax = max(max|w_i|, 1e-8); for r in {6/7, 0.9, 0.95,
+ * 1.0, 1.05, 1.1} (fp32): s = fl32(fl32(amax*r)/7), q_i = clamp(rint(w_i/s),
+ * -8, 7), error = sum_i (w_i - q_i*s)^2 in fp64, index order; the first
+ * candidate with the strictly smallest error wins; scale = bf16_rne(s).
+ * [DeepSeek-V4-Flash-0731-W4A16 model card, "FP4 -> INT4 conversion
+ * algorithm", steps 1-2, and its conversion-script sketch.]
+ *   mxfp4 [N][K/32][17] (4-byte aligned) -> q_out int32 [N][K/8] (16-byte
+ *   aligned), scale_out bfloat16 bits [N][K/32].  Blocks with e >= 253 may
+ *   overflow fp32 and e == 255 is +inf: reject them with moe_validate_mxfp4.
+ */
+int quantize_fp4_to_int4g32(const uint8_t* mxfp4, int N, int K, int32_t* q_out, uint16_t* scale_out,
+                            void* stream);
+
+/* Count MXFP4 blocks whose exponent byte is 0xFF (scale +inf: infinity times
+ * a zero code is NaN, which the ds4 notes treat as an error for E8M0 scales).
+ * Adds the count to *bad_count_dev (device int32, caller zeroes it). */
+int moe_validate_mxfp4(const uint8_t* blocks, int64_t n_blocks, int32_t* bad_count_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_DECODE_H */

@@ -105,7 +105,7 @@ def lib():
 
 
 def default_threads() -> int:
-    return max(1, min(os.cpu_count() or 1, 64))
+    return max(1, min(os.cpu_count() or 1, 16))
 
 
 def _check(rc: int, what: str) -> None:

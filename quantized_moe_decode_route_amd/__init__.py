@@ -1,0 +1,230 @@
+"""Python binding of libmoedecode.so (routed-expert MoE decode for gfx950).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels behind the C ABI declared in ``include/moe_decode.h``.  Functions
+keep the C names; tensors are torch CUDA tensors (device memory) and the
+stream defaults to torch's current stream.  If the shared library has not
+been built, every call raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libmoedecode.so")
+
+MOE_OK = 0
+MOE_FMT_MXFP4, MOE_FMT_Q2K, MOE_FMT_INT4G32 = 0, 1, 2
+FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2k": MOE_FMT_Q2K, "int4g32": MOE_FMT_INT4G32}
+MOE_MAX_TOKENS = 8
+MOE_MAX_TOPK = 8
+
+EXPORTS = (
+    "moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_device_check",
+    "moe_expert_gemv_mxfp4", "moe_expert_gemv_q2k", "moe_expert_gemv_int4g32",
+    "moe_route_workspace_bytes", "moe_route_topk",
+    "moe_layer_workspace_bytes", "moe_workspace_init", "moe_layer_decode", "moe_layer_decode_profiled",
+    "moe_stack_workspace_bytes", "moe_stack_decode", "moe_rmsnorm_bf16",
+    "quantize_fp4_to_int4g32", "moe_validate_mxfp4",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().moe_status_string(status).decode()
+        if status == 4:
+            msg += f" (hipError {lib().moe_last_hip_error()})"
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+class moe_layer_desc(ctypes.Structure):
+    _fields_ = [
+        ("format", ctypes.c_int), ("n_experts", ctypes.c_int), ("d_model", ctypes.c_int),
+        ("d_ff", ctypes.c_int), ("top_k", ctypes.c_int),
+        ("router_w", ctypes.c_void_p),
+        ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+        ("gate_stride", ctypes.c_int64), ("up_stride", ctypes.c_int64), ("down_stride", ctypes.c_int64),
+        ("gate_scale", ctypes.c_void_p), ("up_scale", ctypes.c_void_p), ("down_scale", ctypes.c_void_p),
+        ("gate_scale_stride", ctypes.c_int64), ("up_scale_stride", ctypes.c_int64),
+        ("down_scale_stride", ctypes.c_int64),
+    ]
+
+
+_LIB = None
+_vp, _i, _i64, _sz, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(the HIP library is required; there is no fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "moe_abi_version": (_i, []),
+            "moe_status_string": (ctypes.c_char_p, [_i]),
+            "moe_last_hip_error": (_i, []),
+            "moe_device_check": (_i, []),
+            "moe_expert_gemv_mxfp4": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp]),
+            "moe_expert_gemv_q2k": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp]),
+            "moe_expert_gemv_int4g32": (_i, [_vp, _vp, _i, _i, _vp, _i, _vp, _vp]),
+            "moe_route_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+            "moe_route_topk": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
+            "moe_layer_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+            "moe_workspace_init": (_i, [_vp, _sz, _vp]),
+            "moe_layer_decode": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _sz, _vp, _vp, _vp]),
+            "moe_layer_decode_profiled": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _sz, _vp, _vp,
+                                               ctypes.POINTER(_vp), _vp]),
+            "moe_stack_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+            "moe_stack_decode": (_i, [ctypes.POINTER(moe_layer_desc), _i, _vp, _i, _vp, _d, _vp, _sz, _vp]),
+            "moe_rmsnorm_bf16": (_i, [_vp, _i, _i, _d, _vp, _vp]),
+            "quantize_fp4_to_int4g32": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+            "moe_validate_mxfp4": (_i, [_vp, _i64, _vp, _vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+# ---------------------------------------------------------------- API (C names)
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def moe_device_check() -> None:
+    _check("moe_device_check", lib().moe_device_check())
+
+
+def moe_expert_gemv_mxfp4(blocks, N: int, K: int, x, y, stream=None) -> None:
+    B = x.shape[0]
+    _check("moe_expert_gemv_mxfp4",
+           lib().moe_expert_gemv_mxfp4(_ptr(blocks), N, K, _ptr(x), B, _ptr(y), _stream(stream)))
+
+
+def moe_expert_gemv_q2k(blocks, N: int, K: int, x, y, stream=None) -> None:
+    B = x.shape[0]
+    _check("moe_expert_gemv_q2k",
+           lib().moe_expert_gemv_q2k(_ptr(blocks), N, K, _ptr(x), B, _ptr(y), _stream(stream)))
+
+
+def moe_expert_gemv_int4g32(q, scale, N: int, K: int, x, y, stream=None) -> None:
+    B = x.shape[0]
+    _check("moe_expert_gemv_int4g32",
+           lib().moe_expert_gemv_int4g32(_ptr(q), _ptr(scale), N, K, _ptr(x), B, _ptr(y), _stream(stream)))
+
+
+def moe_route_workspace_bytes(B: int, D: int, E: int, top_k: int) -> int:
+    return lib().moe_route_workspace_bytes(B, D, E, top_k)
+
+
+def moe_route_topk(router_w, x_bf16, top_k: int, idx, gate_w, ws, logits_out=None, stream=None) -> None:
+    E, D = router_w.shape
+    B = x_bf16.shape[0]
+    _check("moe_route_topk",
+           lib().moe_route_topk(_ptr(router_w), E, D, _ptr(x_bf16), B, top_k, _ptr(idx), _ptr(gate_w),
+                                _ptr(logits_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_workspace_bytes(B: int, D: int, F: int, E: int, top_k: int) -> int:
+    return lib().moe_layer_workspace_bytes(B, D, F, E, top_k)
+
+
+def moe_workspace_init(ws, stream=None) -> None:
+    _check("moe_workspace_init",
+           lib().moe_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def make_layer_desc(fmt: str, router_w, gate, up, down, n_experts: int, d_model: int, d_ff: int, top_k: int,
+                    gate_stride: int, up_stride: int, down_stride: int, gate_scale=None, up_scale=None,
+                    down_scale=None, gate_scale_stride: int = 0, up_scale_stride: int = 0,
+                    down_scale_stride: int = 0) -> moe_layer_desc:
+    """Fill the C descriptor; tensors (or raw device addresses) must outlive its use."""
+    d = moe_layer_desc()
+    d.format = FORMATS[fmt]
+    d.n_experts, d.d_model, d.d_ff, d.top_k = n_experts, d_model, d_ff, top_k
+    d.router_w = _ptr(router_w)
+    d.gate, d.up, d.down = _ptr(gate), _ptr(up), _ptr(down)
+    d.gate_stride, d.up_stride, d.down_stride = gate_stride, up_stride, down_stride
+    d.gate_scale, d.up_scale, d.down_scale = _ptr(gate_scale), _ptr(up_scale), _ptr(down_scale)
+    d.gate_scale_stride, d.up_scale_stride, d.down_scale_stride = gate_scale_stride, up_scale_stride, down_scale_stride
+    return d
+
+
+def moe_layer_decode(desc: moe_layer_desc, x_bf16, y, ws, idx_out=None, gw_out=None, stream=None) -> None:
+    B = x_bf16.shape[0]
+    _check("moe_layer_decode",
+           lib().moe_layer_decode(ctypes.byref(desc), _ptr(x_bf16), B, _ptr(y), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _ptr(idx_out), _ptr(gw_out), _stream(stream)))
+
+
+def moe_layer_decode_profiled(desc: moe_layer_desc, x_bf16, y, ws, events, idx_out=None, gw_out=None,
+                              stream=None) -> None:
+    """``events``: 5 raw hipEvent_t handles (ints) or None entries."""
+    B = x_bf16.shape[0]
+    arr = (ctypes.c_void_p * 5)(*[e if e else None for e in events])
+    _check("moe_layer_decode_profiled",
+           lib().moe_layer_decode_profiled(ctypes.byref(desc), _ptr(x_bf16), B, _ptr(y), _ptr(ws),
+                                           ws.numel() * ws.element_size(), _ptr(idx_out), _ptr(gw_out), arr,
+                                           _stream(stream)))
+
+
+def moe_stack_workspace_bytes(B: int, D: int, F: int, E: int, top_k: int) -> int:
+    return lib().moe_stack_workspace_bytes(B, D, F, E, top_k)
+
+
+def moe_stack_decode(descs, h_in, h_out, ws, eps: float = 1e-6, stream=None) -> None:
+    arr = (moe_layer_desc * len(descs))(*descs)
+    B = h_in.shape[0]
+    _check("moe_stack_decode",
+           lib().moe_stack_decode(arr, len(descs), _ptr(h_in), B, _ptr(h_out), eps, _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_rmsnorm_bf16(h, x_out, eps: float = 1e-6, stream=None) -> None:
+    B, D = h.shape
+    _check("moe_rmsnorm_bf16", lib().moe_rmsnorm_bf16(_ptr(h), B, D, eps, _ptr(x_out), _stream(stream)))
+
+
+def quantize_fp4_to_int4g32(mxfp4, N: int, K: int, q_out, scale_out, stream=None) -> None:
+    _check("quantize_fp4_to_int4g32",
+           lib().quantize_fp4_to_int4g32(_ptr(mxfp4), N, K, _ptr(q_out), _ptr(scale_out), _stream(stream)))
+
+
+def moe_validate_mxfp4(blocks, n_blocks: int, bad_count_dev, stream=None) -> None:
+    _check("moe_validate_mxfp4",
+           lib().moe_validate_mxfp4(_ptr(blocks), n_blocks, _ptr(bad_count_dev), _stream(stream)))

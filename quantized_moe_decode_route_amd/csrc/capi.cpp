@@ -1,0 +1,275 @@
+// C ABI of libmoedecode: argument validation, workspace layout and launch
+// sequencing.  No entry point allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip = (int)e;
+  return MOE_ERR_HIP;
+}
+
+int arch_check() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hip_status(hipErrorNoDevice);
+  // Cache per device: the answer cannot change for a device ordinal.
+  static int cached[64] = {0};  // 0 unknown, 1 ok, 2 wrong arch
+  if (dev >= 0 && dev < 64 && cached[dev]) return cached[dev] == 1 ? MOE_OK : MOE_ERR_ARCH;
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_status(e);
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) cached[dev] = ok ? 1 : 2;
+  return ok ? MOE_OK : MOE_ERR_ARCH;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int block_len(int fmt) { return fmt == MOE_FMT_Q2K ? 256 : 32; }
+
+int check_gemv(const void* w, int N, int K, const float* x, int B, float* y, int fmt) {
+  if (!w || !x || !y) return MOE_ERR_ARG;
+  if (N <= 0 || K <= 0) return MOE_ERR_ARG;
+  if (B < 1 || B > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
+  if (K % block_len(fmt) != 0) return MOE_ERR_SHAPE;
+  if (!aligned(x, 16)) return MOE_ERR_ALIGN;
+  if (fmt == MOE_FMT_INT4G32 ? !aligned(w, 16) : !aligned(w, 4)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+int check_layer(const moe_layer_desc* L, int B) {
+  if (!L) return MOE_ERR_ARG;
+  if (L->format < MOE_FMT_MXFP4 || L->format > MOE_FMT_INT4G32) return MOE_ERR_ARG;
+  if (!L->router_w || !L->gate || !L->up || !L->down) return MOE_ERR_ARG;
+  if (L->n_experts < 1 || L->n_experts > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
+  if (L->top_k < 1 || L->top_k > MOE_MAX_TOPK || L->top_k > L->n_experts) return MOE_ERR_SHAPE;
+  if (B < 1 || B > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
+  const int bl = block_len(L->format);
+  if (L->d_model <= 0 || L->d_ff <= 0 || L->d_model % bl || L->d_ff % bl) return MOE_ERR_SHAPE;
+  if (L->gate_stride < 0 || L->up_stride < 0 || L->down_stride < 0) return MOE_ERR_ARG;
+  if (!aligned(L->router_w, 16)) return MOE_ERR_ALIGN;
+  const uintptr_t wa = L->format == MOE_FMT_INT4G32 ? 16 : 4;
+  if (!aligned(L->gate, wa) || !aligned(L->up, wa) || !aligned(L->down, wa)) return MOE_ERR_ALIGN;
+  if (L->gate_stride % wa || L->up_stride % wa || L->down_stride % wa) return MOE_ERR_ALIGN;
+  if (L->format == MOE_FMT_INT4G32) {
+    if (!L->gate_scale || !L->up_scale || !L->down_scale) return MOE_ERR_ARG;
+    if (!aligned(L->gate_scale, 2) || !aligned(L->up_scale, 2) || !aligned(L->down_scale, 2)) return MOE_ERR_ALIGN;
+    if (L->gate_scale_stride % 2 || L->up_scale_stride % 2 || L->down_scale_stride % 2) return MOE_ERR_ALIGN;
+  }
+  return MOE_OK;
+}
+
+WeightRef wref(const void* base, int64_t stride, const uint16_t* scale, int64_t scale_stride) {
+  WeightRef w;
+  w.base = static_cast<const uint8_t*>(base);
+  w.stride = stride;
+  w.scale = scale;
+  w.scale_stride = scale_stride;
+  return w;
+}
+
+int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, const float* residual, void* ws,
+               size_t ws_bytes, int32_t* idx_out, float* gw_out, void* const* events, hipStream_t s) {
+  const int D = L->d_model, F = L->d_ff, E = L->n_experts, k = L->top_k;
+  const WsLayout W = layer_ws_layout(B, D, F, E, k);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  auto rec = [&](int i) -> hipError_t {
+    if (events && events[i]) return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+    return hipSuccess;
+  };
+  hipError_t e;
+  if ((e = rec(0)) != hipSuccess) return hip_status(e);
+  if ((e = launch_route(L->router_w, E, D, x_bf16, B, k, w, W, idx_out, gw_out, nullptr, s)) != hipSuccess)
+    return hip_status(e);
+  if ((e = rec(1)) != hipSuccess) return hip_status(e);
+  const WeightRef g = wref(L->gate, L->gate_stride, L->gate_scale, L->gate_scale_stride);
+  const WeightRef u = wref(L->up, L->up_stride, L->up_scale, L->up_scale_stride);
+  const WeightRef d = wref(L->down, L->down_stride, L->down_scale, L->down_scale_stride);
+  if ((e = launch_gate_up(L->format, g, u, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
+  if ((e = rec(2)) != hipSuccess) return hip_status(e);
+  if ((e = launch_down(L->format, d, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
+  if ((e = rec(3)) != hipSuccess) return hip_status(e);
+  if ((e = launch_combine(D, B, k, w, W, y, residual, s)) != hipSuccess) return hip_status(e);
+  if ((e = rec(4)) != hipSuccess) return hip_status(e);
+  (void)ws_bytes;
+  return MOE_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  if (have < need) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument (null pointer or bad size)";
+    case MOE_ERR_SHAPE: return "unsupported shape (block multiple, token count, top_k or expert count)";
+    case MOE_ERR_ARCH: return "device is not gfx950";
+    case MOE_ERR_HIP: return "HIP runtime error (see moe_last_hip_error)";
+    case MOE_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case MOE_ERR_ALIGN: return "pointer or stride misaligned";
+    default: return "unknown status";
+  }
+}
+
+int moe_last_hip_error(void) { return g_last_hip; }
+
+int moe_device_check(void) { return arch_check(); }
+
+int moe_expert_gemv_mxfp4(const uint8_t* blocks, int N, int K, const float* x, int B, float* y, void* stream) {
+  int st = check_gemv(blocks, N, K, x, B, y, MOE_FMT_MXFP4);
+  if (st != MOE_OK) return st;
+  if ((st = arch_check()) != MOE_OK) return st;
+  return hip_status(launch_gemv(MOE_FMT_MXFP4, blocks, nullptr, N, K, x, B, y, (hipStream_t)stream));
+}
+
+int moe_expert_gemv_q2k(const uint8_t* blocks, int N, int K, const float* x, int B, float* y, void* stream) {
+  int st = check_gemv(blocks, N, K, x, B, y, MOE_FMT_Q2K);
+  if (st != MOE_OK) return st;
+  if ((st = arch_check()) != MOE_OK) return st;
+  return hip_status(launch_gemv(MOE_FMT_Q2K, blocks, nullptr, N, K, x, B, y, (hipStream_t)stream));
+}
+
+int moe_expert_gemv_int4g32(const int32_t* q, const uint16_t* scale_bf16, int N, int K, const float* x, int B,
+                            float* y, void* stream) {
+  int st = check_gemv(q, N, K, x, B, y, MOE_FMT_INT4G32);
+  if (st != MOE_OK) return st;
+  if (!scale_bf16) return MOE_ERR_ARG;
+  if (!aligned(scale_bf16, 2)) return MOE_ERR_ALIGN;
+  if ((st = arch_check()) != MOE_OK) return st;
+  return hip_status(launch_gemv(MOE_FMT_INT4G32, q, scale_bf16, N, K, x, B, y, (hipStream_t)stream));
+}
+
+size_t moe_route_workspace_bytes(int B, int D, int E, int top_k) {
+  if (B < 1 || D < 1 || E < 1 || top_k < 1) return 0;
+  // Routing uses the leading regions of a layer workspace, up to the
+  // activation widened to fp32 (the region before h).
+  return layer_ws_layout(B, D, 0, E, top_k).h;
+}
+
+int moe_route_topk(const float* router_w, int E, int D, const uint16_t* x_bf16, int B, int top_k, int32_t* idx,
+                   float* gate_w, double* logits_out, void* ws, size_t ws_bytes, void* stream) {
+  if (!router_w || !x_bf16 || !idx || !gate_w) return MOE_ERR_ARG;
+  if (E < 1 || E > MOE_MAX_EXPERTS || D <= 0) return MOE_ERR_SHAPE;
+  if (B < 1 || B > MOE_MAX_TOKENS || top_k < 1 || top_k > MOE_MAX_TOPK || top_k > E) return MOE_ERR_SHAPE;
+  if (D % 4 != 0) return MOE_ERR_SHAPE;
+  if (!aligned(router_w, 16) || !aligned(x_bf16, 8)) return MOE_ERR_ALIGN;
+  // The route kernel also widens x into the xf region, which needs D.
+  const WsLayout W = layer_ws_layout(B, D, 0, E, top_k);
+  int st = check_ws(ws, ws_bytes, W.h);
+  if (st != MOE_OK) return st;
+  if ((st = arch_check()) != MOE_OK) return st;
+  return hip_status(launch_route(router_w, E, D, x_bf16, B, top_k, static_cast<uint8_t*>(ws), W, idx, gate_w,
+                                 logits_out, (hipStream_t)stream));
+}
+
+size_t moe_layer_workspace_bytes(int B, int D, int F, int E, int top_k) {
+  if (B < 1 || D < 1 || F < 1 || E < 1 || top_k < 1) return 0;
+  return layer_ws_layout(B, D, F, E, top_k).total;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes < 64 * sizeof(uint32_t) || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  int st = arch_check();
+  if (st != MOE_OK) return st;
+  // Counters sit at the start of every workspace layout.
+  return hip_status(launch_zero_u32(static_cast<uint32_t*>(ws), 64, (hipStream_t)stream));
+}
+
+int moe_layer_decode(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws, size_t ws_bytes,
+                     int32_t* idx_out, float* gw_out, void* stream) {
+  return moe_layer_decode_profiled(L, x_bf16, B, y, ws, ws_bytes, idx_out, gw_out, nullptr, stream);
+}
+
+int moe_layer_decode_profiled(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
+                              size_t ws_bytes, int32_t* idx_out, float* gw_out, void* const* events, void* stream) {
+  int st = check_layer(L, B);
+  if (st != MOE_OK) return st;
+  if (!x_bf16 || !y) return MOE_ERR_ARG;
+  if (!aligned(x_bf16, 8) || !aligned(y, 16)) return MOE_ERR_ALIGN;
+  const size_t need = layer_ws_layout(B, L->d_model, L->d_ff, L->n_experts, L->top_k).total;
+  if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
+  if ((st = arch_check()) != MOE_OK) return st;
+  return layer_impl(L, x_bf16, B, y, nullptr, ws, ws_bytes, idx_out, gw_out, events, (hipStream_t)stream);
+}
+
+size_t moe_stack_workspace_bytes(int B, int D, int F, int E, int top_k) {
+  const size_t layer = moe_layer_workspace_bytes(B, D, F, E, top_k);
+  if (!layer) return 0;
+  // + normalised activation (bf16) of the current layer
+  return layer + align256((size_t)B * D * sizeof(uint16_t));
+}
+
+int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* h_in, int B, float* h_out, double eps,
+                     void* ws, size_t ws_bytes, void* stream) {
+  if (!layers || n_layers < 1 || !h_in || !h_out) return MOE_ERR_ARG;
+  if (!(eps >= 0.0)) return MOE_ERR_ARG;
+  int st;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_layer(&layers[l], B)) != MOE_OK) return st;
+    if (layers[l].d_model != layers[0].d_model || layers[l].d_ff != layers[0].d_ff ||
+        layers[l].n_experts != layers[0].n_experts || layers[l].top_k != layers[0].top_k)
+      return MOE_ERR_SHAPE;
+  }
+  if (!aligned(h_in, 16) || !aligned(h_out, 16)) return MOE_ERR_ALIGN;
+  const int D = layers[0].d_model;
+  const size_t layer_bytes = moe_layer_workspace_bytes(B, D, layers[0].d_ff, layers[0].n_experts, layers[0].top_k);
+  if ((st = check_ws(ws, ws_bytes, moe_stack_workspace_bytes(B, D, layers[0].d_ff, layers[0].n_experts,
+                                                            layers[0].top_k))) != MOE_OK)
+    return st;
+  if ((st = arch_check()) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* xb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + layer_bytes);
+  const float* cur = h_in;
+  for (int l = 0; l < n_layers; ++l) {
+    hipError_t e = launch_rmsnorm_bf16(cur, B, D, eps, xb, s);
+    if (e != hipSuccess) return hip_status(e);
+    st = layer_impl(&layers[l], xb, B, h_out, cur, ws, layer_bytes, nullptr, nullptr, nullptr, s);
+    if (st != MOE_OK) return st;
+    cur = h_out;
+  }
+  return MOE_OK;
+}
+
+int moe_rmsnorm_bf16(const float* h, int B, int D, double eps, uint16_t* x_out, void* stream) {
+  if (!h || !x_out || B < 1 || D < 1) return MOE_ERR_ARG;
+  if (!(eps >= 0.0)) return MOE_ERR_ARG;
+  int st = arch_check();
+  if (st != MOE_OK) return st;
+  return hip_status(launch_rmsnorm_bf16(h, B, D, eps, x_out, (hipStream_t)stream));
+}
+
+int quantize_fp4_to_int4g32(const uint8_t* mxfp4, int N, int K, int32_t* q_out, uint16_t* scale_out, void* stream) {
+  if (!mxfp4 || !q_out || !scale_out || N <= 0 || K <= 0) return MOE_ERR_ARG;
+  if (K % 32) return MOE_ERR_SHAPE;
+  if (!aligned(mxfp4, 4) || !aligned(q_out, 16) || !aligned(scale_out, 2)) return MOE_ERR_ALIGN;
+  int st = arch_check();
+  if (st != MOE_OK) return st;
+  return hip_status(launch_quantize_int4(mxfp4, (int64_t)N * (K / 32), q_out, scale_out, (hipStream_t)stream));
+}
+
+int moe_validate_mxfp4(const uint8_t* blocks, int64_t n_blocks, int32_t* bad_count_dev, void* stream) {
+  if (!blocks || !bad_count_dev || n_blocks < 0) return MOE_ERR_ARG;
+  int st = arch_check();
+  if (st != MOE_OK) return st;
+  return hip_status(launch_validate_mxfp4(blocks, n_blocks, bad_count_dev, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,200 @@
+// Internal declarations shared by the HIP translation units of libmoedecode.
+// Device helpers for the three weight formats, wave reductions, workspace
+// layout and the host-side launch functions each .hip file defines.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_decode.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxTok = MOE_MAX_TOKENS;
+constexpr int kMaxTopK = MOE_MAX_TOPK;
+constexpr int kMaxSlots = kMaxTok * kMaxTopK;  // (token, rank) pairs per layer call
+
+// ---------------------------------------------------------------- format helpers
+
+// E8M0 scale as fp32: the bit pattern e<<23, with e == 0 mapped to the
+// subnormal 2^-127 (0x00400000) and e == 255 giving +inf.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
+// One MXFP4 block at byte offset `o` of a 4-byte aligned row: the 17 bytes
+// lie in the five dwords starting at o & ~3.  Returns the exponent byte and
+// the 16 code bytes as four dwords (code byte j in byte j%4 of q[j/4]).
+struct MxRaw {
+  uint32_t d[5];
+  uint32_t sh;  // o & 3
+};
+
+__device__ __forceinline__ void mx_load(const uint8_t* __restrict__ row, uint32_t o, MxRaw& r) {
+  const uint32_t a = o & ~3u;
+  const uint4 v = *reinterpret_cast<const uint4*>(__builtin_assume_aligned(row + a, 4));
+  r.d[0] = v.x;
+  r.d[1] = v.y;
+  r.d[2] = v.z;
+  r.d[3] = v.w;
+  r.d[4] = *reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(row + a + 16, 4));
+  r.sh = o & 3u;
+}
+
+// Codes start at byte sh+1 (1..4) of the five-dword window; v_perm selects
+// four consecutive bytes of (hi:lo), including the whole `hi` dword when the
+// shift is 4.
+__device__ __forceinline__ void mx_unpack(const MxRaw& r, uint32_t& e, uint32_t q[4]) {
+  e = (r.d[0] >> (8 * r.sh)) & 0xFFu;
+  const uint32_t sel = 0x03020100u + (r.sh + 1) * 0x01010101u;
+  q[0] = __builtin_amdgcn_perm(r.d[1], r.d[0], sel);
+  q[1] = __builtin_amdgcn_perm(r.d[2], r.d[1], sel);
+  q[2] = __builtin_amdgcn_perm(r.d[3], r.d[2], sel);
+  q[3] = __builtin_amdgcn_perm(r.d[4], r.d[3], sel);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two E2M1 values of code byte `sel` of dword q: .x = low nibble, .y = high
+// nibble (gfx950 v_cvt_scalef32_pk_f32_fp4 with scale 1).
+#define MOE_FP4X2(q, sel) __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((q), 1.0f, (sel))
+
+// Sum over the 32 weights of one MXFP4 block of E2M1[c_i] * x_i (scale not
+// applied).  Element 2j is the high nibble of code byte j.
+__device__ __forceinline__ float mx_block_dot(const uint32_t q[4], const float* __restrict__ x32) {
+  float acc = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float4 xa = *reinterpret_cast<const float4*>(x32 + 8 * w);
+    const float4 xb = *reinterpret_cast<const float4*>(x32 + 8 * w + 4);
+    const f32x2 p0 = MOE_FP4X2(q[w], 0);
+    const f32x2 p1 = MOE_FP4X2(q[w], 1);
+    const f32x2 p2 = MOE_FP4X2(q[w], 2);
+    const f32x2 p3 = MOE_FP4X2(q[w], 3);
+    acc = __builtin_fmaf(p0.y, xa.x, acc);
+    acc = __builtin_fmaf(p0.x, xa.y, acc);
+    acc = __builtin_fmaf(p1.y, xa.z, acc);
+    acc = __builtin_fmaf(p1.x, xa.w, acc);
+    acc = __builtin_fmaf(p2.y, xb.x, acc);
+    acc = __builtin_fmaf(p2.x, xb.y, acc);
+    acc = __builtin_fmaf(p3.y, xb.z, acc);
+    acc = __builtin_fmaf(p3.x, xb.w, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h16);
+}
+
+// fp32 -> bfloat16 bits, round to nearest even (finite inputs; NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// ---------------------------------------------------------------- workspace
+
+// One unique expert of a layer call and the (token, rank) pairs routed to it,
+// tokens ascending.
+struct ExpertGroup {
+  int32_t expert;
+  int32_t n;
+  int32_t tok[kMaxTok];
+  int32_t slot[kMaxTok];  // rank j of the expert in that token's top-k
+  int32_t pad[2];
+};
+static_assert(sizeof(ExpertGroup) == 80, "group record layout");
+
+// Byte offsets of the regions of a layer workspace (each 256-byte aligned).
+struct WsLayout {
+  size_t counters;  // uint32[64]: zeroed by moe_workspace_init, left zero by every call
+  size_t logits;    // fp64 [B][E]
+  size_t idx;       // int32 [B][k]
+  size_t gw;        // fp32 [B][k]
+  size_t ngroups;   // int32 [1]: number of unique experts U
+  size_t groups;    // ExpertGroup [B*k]
+  size_t xf;        // fp32 [B][D]: the activation widened from bfloat16
+  size_t h;         // fp32 [B][k][F]: SiLU(gate) * up per (token, rank)
+  size_t yp;        // fp32 [B][k][D]: down projection per (token, rank)
+  size_t total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline WsLayout layer_ws_layout(int B, int D, int F, int E, int k) {
+  WsLayout L;
+  size_t o = 0;
+  L.counters = o; o = align256(o + 64 * sizeof(uint32_t));
+  L.logits = o;   o = align256(o + (size_t)B * E * sizeof(double));
+  L.idx = o;      o = align256(o + (size_t)B * k * sizeof(int32_t));
+  L.gw = o;       o = align256(o + (size_t)B * k * sizeof(float));
+  L.ngroups = o;  o = align256(o + sizeof(int32_t));
+  L.groups = o;   o = align256(o + (size_t)B * k * sizeof(ExpertGroup));
+  L.xf = o;       o = align256(o + (size_t)B * D * sizeof(float));
+  L.h = o;        o = align256(o + (size_t)B * k * F * sizeof(float));
+  L.yp = o;       o = align256(o + (size_t)B * k * D * sizeof(float));
+  L.total = o;
+  return L;
+}
+
+// Counter slots inside the counters region.
+enum : int { kCtrRoute = 0 };
+
+// ---------------------------------------------------------------- launchers
+// Each returns a hipError_t (hipSuccess on success).
+
+struct WeightRef {
+  const uint8_t* base;      // MXFP4 / Q2_K blocks or INT4 code words
+  const uint16_t* scale;    // INT4 scales (else null)
+  int64_t stride;           // bytes between experts
+  int64_t scale_stride;     // bytes between experts' scales
+};
+
+hipError_t launch_gemv(int fmt, const void* w0, const uint16_t* scale, int N, int K, const float* x,
+                       int B, float* y, hipStream_t s);
+
+hipError_t launch_route(const float* router_w, int E, int D, const uint16_t* x_bf16, int B, int k,
+                        uint8_t* ws, const WsLayout& L, int32_t* idx_out, float* gw_out,
+                        double* logits_out, hipStream_t s);
+
+hipError_t launch_gate_up(int fmt, const WeightRef& gate, const WeightRef& up, int D, int F, int B,
+                          int k, uint8_t* ws, const WsLayout& L, hipStream_t s);
+
+hipError_t launch_down(int fmt, const WeightRef& down, int D, int F, int B, int k, uint8_t* ws,
+                       const WsLayout& L, hipStream_t s);
+
+hipError_t launch_combine(int D, int B, int k, const uint8_t* ws, const WsLayout& L, float* y,
+                          const float* residual, hipStream_t s);
+
+hipError_t launch_rmsnorm_bf16(const float* h, int B, int D, double eps, uint16_t* out, hipStream_t s);
+
+hipError_t launch_quantize_int4(const uint8_t* mx, int64_t ngroups, int32_t* q, uint16_t* scale,
+                                hipStream_t s);
+
+hipError_t launch_validate_mxfp4(const uint8_t* blocks, int64_t n, int32_t* bad, hipStream_t s);
+
+hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
+
+}  // namespace moe

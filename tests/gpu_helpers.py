@@ -1,0 +1,140 @@
+"""Shared set-up for the GPU parity tests: device tensors, synthetic layers
+built on the GPU with the seeded fill, and the oracle-side twin that
+regenerates only the experts a call actually uses.
+
+Expected values always come from ``oracle`` on inputs produced by ``synth``
+(never from the HIP path)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import quantized_moe_decode_route_amd as moe
+import synth
+
+BLOCK = {"mxfp4": (32, 17), "q2k": (256, 84)}
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    """numpy -> device tensor with the same bytes (uint16 travels as int16)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a.copy()).to("cuda")
+
+
+def host(t: torch.Tensor, dtype=None) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    return a.view(dtype) if dtype is not None else a
+
+
+def rel_inf_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
+    """Per row: max |gpu - ref| / max |ref|."""
+    y_gpu = np.asarray(y_gpu, dtype=np.float64).reshape(y_ref.shape)
+    num = np.max(np.abs(y_gpu - y_ref), axis=-1)
+    den = np.max(np.abs(y_ref), axis=-1)
+    return num / np.where(den == 0, 1.0, den)
+
+
+TOL = 1e-4  # max |err| <= 1e-4 * ||y||_inf per token, fp32-accumulated outputs
+
+
+def assert_parity(y_gpu, y_ref, tol=TOL, what=""):
+    e = rel_inf_err(y_gpu, y_ref)
+    assert np.all(e <= tol), f"{what}: max rel-inf error {e.max():.3e} > {tol}"
+    return float(e.max())
+
+
+def matrix_bytes(fmt: str, n: int, k: int) -> int:
+    bw, bb = BLOCK[fmt]
+    return n * (k // bw) * bb
+
+
+class Layer:
+    """One MoE layer with E experts resident on the GPU, seeded.
+
+    fmt "mxfp4" / "q2k": weights filled on the GPU by synth.gpu_fill.
+    fmt "int4g32": MXFP4 weights filled on the GPU, then converted by
+    quantize_fp4_to_int4g32 (the conversion under test elsewhere); the oracle
+    side converts its own twin bytes with oracle.quantize_fp4_to_int4g32.
+    """
+
+    def __init__(self, fmt: str, seed: int, layer: int, E: int, D: int, F: int, top_k: int = 6):
+        self.fmt, self.seed, self.layer = fmt, seed, layer
+        self.E, self.D, self.F, self.k = E, D, F, top_k
+        self.router = synth.router_weights(seed, layer, E, D)
+        self.router_dev = dev(self.router)
+        src = "mxfp4" if fmt == "int4g32" else fmt
+        self.src = src
+        self.bytes = {}
+        stream = torch.cuda.current_stream().cuda_stream
+        for proj, (n, kk) in ((synth.PROJ_GATE, (F, D)), (synth.PROJ_UP, (F, D)), (synth.PROJ_DOWN, (D, F))):
+            per = matrix_bytes(src, n, kk)
+            stride = (per + 255) // 256 * 256
+            buf = torch.empty(E * stride, dtype=torch.uint8, device="cuda")
+            bw, bb = BLOCK[src]
+            for e in range(E):
+                synth.gpu_fill(src, buf.data_ptr() + e * stride, seed, layer, e, 1, proj,
+                               n * (kk // bw), stream)
+            self.bytes[proj] = (buf, stride)
+        if fmt == "int4g32":
+            self.q = {}
+            for proj, (n, kk) in ((synth.PROJ_GATE, (F, D)), (synth.PROJ_UP, (F, D)), (synth.PROJ_DOWN, (D, F))):
+                buf, stride = self.bytes[proj]
+                qstride = n * kk // 2
+                sstride = (n * (kk // 32) * 2 + 255) // 256 * 256
+                q = torch.empty(E * qstride, dtype=torch.uint8, device="cuda")
+                s = torch.empty(E * sstride, dtype=torch.uint8, device="cuda")
+                for e in range(E):
+                    moe.quantize_fp4_to_int4g32(buf.data_ptr() + e * stride, n, kk, q.data_ptr() + e * qstride,
+                                                s.data_ptr() + e * sstride)
+                self.q[proj] = (q, qstride, s, sstride)
+            del self.bytes
+            torch.cuda.synchronize()
+            self.desc = moe.make_layer_desc(
+                fmt, self.router_dev, self.q[0][0], self.q[1][0], self.q[2][0], E, D, F, top_k,
+                self.q[0][1], self.q[1][1], self.q[2][1], self.q[0][2], self.q[1][2], self.q[2][2],
+                self.q[0][3], self.q[1][3], self.q[2][3])
+        else:
+            self.desc = moe.make_layer_desc(
+                fmt, self.router_dev, self.bytes[0][0], self.bytes[1][0], self.bytes[2][0], E, D, F, top_k,
+                self.bytes[0][1], self.bytes[1][1], self.bytes[2][1])
+        self._cache = {}
+
+    # -- oracle side: regenerate expert e's bytes with the host twin
+    def expert_host(self, e: int):
+        if e in self._cache:
+            return self._cache[e]
+        D, F = self.D, self.F
+        mats = []
+        for proj, (n, kk) in ((synth.PROJ_GATE, (F, D)), (synth.PROJ_UP, (F, D)), (synth.PROJ_DOWN, (D, F))):
+            b = synth.expert_tensor(self.src, self.seed, self.layer, e, proj, n, kk)
+            if self.fmt == "int4g32":
+                b = oracle.quantize_fp4_to_int4g32(b, n, kk)
+            mats.append(b)
+        self._cache[e] = tuple(mats)
+        return self._cache[e]
+
+    def workspace(self, B: int) -> torch.Tensor:
+        nbytes = moe.moe_layer_workspace_bytes(B, self.D, self.F, self.E, self.k)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        assert ws.data_ptr() % 256 == 0
+        moe.moe_workspace_init(ws)
+        return ws
+
+    def run(self, x_bf16: np.ndarray, ws=None):
+        B = x_bf16.shape[0]
+        ws = ws if ws is not None else self.workspace(B)
+        x = dev(x_bf16)
+        y = torch.empty((B, self.D), dtype=torch.float32, device="cuda")
+        idx = torch.empty((B, self.k), dtype=torch.int32, device="cuda")
+        gw = torch.empty((B, self.k), dtype=torch.float32, device="cuda")
+        moe.moe_layer_decode(self.desc, x, y, ws, idx, gw)
+        torch.cuda.synchronize()
+        return host(y), host(idx), host(gw)
+
+    def oracle(self, x_bf16: np.ndarray):
+        return oracle.layer_decode(self.fmt, self.expert_host, self.router, x_bf16, self.k, self.F)

@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports every function include/moe_decode.h
+declares, and rejects bad arguments on the host before any GPU work.  No
+compute call is made here (these tests run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_moe_decode_route_amd as moe
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "moe_decode.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from quantized_moe_decode_route_amd import _build
+        _build.build()
+    return moe.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s+([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("moe_route_topk", "moe_expert_gemv_mxfp4", "moe_expert_gemv_q2k", "moe_expert_gemv_int4g32",
+                     "moe_layer_decode", "quantize_fp4_to_int4g32"):
+        assert required in names
+    assert set(names) == set(moe.EXPORTS), set(names) ^ set(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings(L):
+    assert moe.moe_abi_version() == 1
+    for st in range(7):
+        assert moe.moe_status_string(st)
+    assert moe.moe_status_string(0) == "ok"
+
+
+def test_workspace_sizes(L):
+    a = moe.moe_layer_workspace_bytes(1, 4096, 2048, 256, 6)
+    b = moe.moe_layer_workspace_bytes(8, 4096, 2048, 256, 6)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+    # h [8][6][2048] and yp [8][6][4096] fp32 dominate at B=8
+    assert b >= 8 * 6 * (2048 + 4096) * 4
+    assert moe.moe_layer_workspace_bytes(0, 4096, 2048, 256, 6) == 0
+    assert moe.moe_route_workspace_bytes(8, 4096, 256, 6) < b
+    assert moe.moe_stack_workspace_bytes(8, 4096, 2048, 256, 6) > b
+
+
+FAKE = 0x1000  # a host-side stand-in address: never dereferenced by validation
+
+
+def test_gemv_argument_validation_on_host(L):
+    assert L.moe_expert_gemv_mxfp4(None, 8, 64, FAKE, 1, FAKE, None) == 1          # null weights
+    assert L.moe_expert_gemv_mxfp4(FAKE, 8, 48, FAKE, 1, FAKE, None) == 2          # K % 32
+    assert L.moe_expert_gemv_mxfp4(FAKE, 8, 64, FAKE, 9, FAKE, None) == 2          # B > 8
+    assert L.moe_expert_gemv_mxfp4(FAKE, 8, 64, FAKE, 0, FAKE, None) == 2          # B < 1
+    assert L.moe_expert_gemv_mxfp4(FAKE, 8, 64, FAKE + 4, 1, FAKE, None) == 6      # x misaligned
+    assert L.moe_expert_gemv_q2k(FAKE, 8, 128, FAKE, 1, FAKE, None) == 2           # K % 256
+    assert L.moe_expert_gemv_int4g32(FAKE + 4, FAKE, 8, 64, FAKE, 1, FAKE, None) == 6  # codes misaligned
+    assert L.moe_expert_gemv_int4g32(FAKE, None, 8, 64, FAKE, 1, FAKE, None) == 1  # null scales
+
+
+def test_layer_and_route_validation_on_host(L):
+    d = moe.make_layer_desc("mxfp4", FAKE, FAKE, FAKE, FAKE, 256, 4096, 2048, 6, 4456704, 4456704, 4456704)
+    ws_ok = 1 << 30
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 9, FAKE, FAKE, ws_ok, None, None, None) == 2   # B > 8
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, None, ws_ok, None, None, None) == 5  # no ws
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE + 16, ws_ok, None, None, None) == 5
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, 1024, None, None, None) == 5   # too small
+    d.top_k = 9
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, ws_ok, None, None, None) == 2
+    d.top_k, d.d_model = 6, 4016   # not a multiple of 32
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, ws_ok, None, None, None) == 2
+    d.d_model, d.format = 4096, 1   # Q2_K needs multiples of 256: 4096 and 2048 are fine
+    d.gate_stride = 2752514         # but strides must keep 4-byte alignment
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, ws_ok, None, None, None) == 6
+    d.format, d.gate_stride = 2, 4194304
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, ws_ok, None, None, None) == 1  # no scales
+    assert L.moe_layer_decode(None, FAKE, 1, FAKE, FAKE, ws_ok, None, None, None) == 1
+    assert L.moe_route_topk(FAKE, 300, 64, FAKE, 1, 6, FAKE, FAKE, None, FAKE, ws_ok, None) == 2   # E > 256
+    assert L.moe_route_topk(FAKE, 256, 64, FAKE, 1, 0, FAKE, FAKE, None, FAKE, ws_ok, None) == 2   # top_k < 1
+    assert L.moe_route_topk(FAKE, 4, 64, FAKE, 1, 6, FAKE, FAKE, None, FAKE, ws_ok, None) == 2     # top_k > E
+    assert L.moe_stack_decode(None, 1, FAKE, 1, FAKE, 1e-6, FAKE, ws_ok, None) == 1
+    assert L.quantize_fp4_to_int4g32(FAKE, 8, 48, FAKE, FAKE, None) == 2
+    assert L.quantize_fp4_to_int4g32(FAKE, 8, 64, FAKE + 4, FAKE, None) == 6
+    assert L.moe_validate_mxfp4(FAKE, -1, FAKE, None) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_LIB", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        moe.moe_abi_version()
