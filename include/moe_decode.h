@@ -146,12 +146,22 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * [B][top_k] and gw_out fp32 [B][top_k] receive the routing if not NULL. */
 int moe_layer_decode(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
                      size_t ws_bytes, int32_t* idx_out, float* gw_out, void* stream);
-/* Same, recording 5 hipEvent_t (passed as void*) on `stream`: before
- * routing, after routing, after gate/up, after down, after the combine.
- * For per-kernel timing only; events may be NULL to skip a record. */
+/* Same, recording two hipEvent_t (passed as void*) on `stream` right before
+ * and right after the layer's kernels, for timing.  Either may be NULL. */
 int moe_layer_decode_profiled(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
                               void* ws, size_t ws_bytes, int32_t* idx_out, float* gw_out,
                               void* const* events, void* stream);
+
+/* Diagnostic: the same layer decode with per-phase wall-clock stamps.  With
+ * trace == NULL only *trace_blocks is set: the number of workgroups of the
+ * single-launch kernel (0 if the shape runs as separate launches, which are
+ * not traced).  Otherwise trace (device, uint64 [*trace_blocks][10]) receives,
+ * per workgroup, the 100 MHz wall clock at: start, own router logits
+ * published, top-k and grouping done, gate/up done, h slice gathered, down
+ * done, partial outputs published, end; then the workgroup's XCD and the
+ * raw value of its XCD arrival counter. */
+int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
+                            size_t ws_bytes, uint64_t* trace, int* trace_blocks, void* stream);
 
 /* ------------------------------------------------------------------ layer stack
  * Residual stream through n_layers MoE layers: for l = 0..n_layers-1,

@@ -25,6 +25,7 @@ EXPORTS = (
     "moe_expert_gemv_mxfp4", "moe_expert_gemv_q2k", "moe_expert_gemv_int4g32",
     "moe_route_workspace_bytes", "moe_route_topk",
     "moe_layer_workspace_bytes", "moe_workspace_init", "moe_layer_decode", "moe_layer_decode_profiled",
+    "moe_layer_decode_traced",
     "moe_stack_workspace_bytes", "moe_stack_decode", "moe_rmsnorm_bf16",
     "quantize_fp4_to_int4g32", "moe_validate_mxfp4",
 )
@@ -78,6 +79,8 @@ def lib() -> ctypes.CDLL:
             "moe_layer_decode": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _sz, _vp, _vp, _vp]),
             "moe_layer_decode_profiled": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _sz, _vp, _vp,
                                                ctypes.POINTER(_vp), _vp]),
+            "moe_layer_decode_traced": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _sz, _vp,
+                                             ctypes.POINTER(_i), _vp]),
             "moe_stack_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
             "moe_stack_decode": (_i, [ctypes.POINTER(moe_layer_desc), _i, _vp, _i, _vp, _d, _vp, _sz, _vp]),
             "moe_rmsnorm_bf16": (_i, [_vp, _i, _i, _d, _vp, _vp]),
@@ -194,13 +197,34 @@ def moe_layer_decode(desc: moe_layer_desc, x_bf16, y, ws, idx_out=None, gw_out=N
 
 def moe_layer_decode_profiled(desc: moe_layer_desc, x_bf16, y, ws, events, idx_out=None, gw_out=None,
                               stream=None) -> None:
-    """``events``: 5 raw hipEvent_t handles (ints) or None entries."""
+    """``events``: 2 raw hipEvent_t handles (ints) or None: before and after the layer."""
     B = x_bf16.shape[0]
-    arr = (ctypes.c_void_p * 5)(*[e if e else None for e in events])
+    arr = (ctypes.c_void_p * 2)(*[e if e else None for e in events])
     _check("moe_layer_decode_profiled",
            lib().moe_layer_decode_profiled(ctypes.byref(desc), _ptr(x_bf16), B, _ptr(y), _ptr(ws),
                                            ws.numel() * ws.element_size(), _ptr(idx_out), _ptr(gw_out), arr,
                                            _stream(stream)))
+
+
+def moe_layer_decode_traced(desc: moe_layer_desc, x_bf16, y, ws, stream=None):
+    """Run the layer and return per-workgroup records (int64 [blocks, 10]: eight
+    100 MHz phase stamps, the XCD, the XCD arrival counter) as a device
+    tensor, or None if the shape is not traced."""
+    import torch
+    B = x_bf16.shape[0]
+    nb = ctypes.c_int(0)
+    _check("moe_layer_decode_traced",
+           lib().moe_layer_decode_traced(ctypes.byref(desc), _ptr(x_bf16), B, _ptr(y), _ptr(ws),
+                                         ws.numel() * ws.element_size(), None, ctypes.byref(nb), _stream(stream)))
+    if nb.value == 0:
+        moe_layer_decode(desc, x_bf16, y, ws, stream=stream)
+        return None
+    tr = torch.zeros((nb.value, 10), dtype=torch.int64, device=x_bf16.device)
+    _check("moe_layer_decode_traced",
+           lib().moe_layer_decode_traced(ctypes.byref(desc), _ptr(x_bf16), B, _ptr(y), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _ptr(tr), ctypes.byref(nb),
+                                         _stream(stream)))
+    return tr
 
 
 def moe_stack_workspace_bytes(B: int, D: int, F: int, E: int, top_k: int) -> int:

@@ -77,7 +77,7 @@ WeightRef wref(const void* base, int64_t stride, const uint16_t* scale, int64_t 
 }
 
 int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, const float* residual, void* ws,
-               size_t ws_bytes, int32_t* idx_out, float* gw_out, void* const* events, hipStream_t s) {
+               int32_t* idx_out, float* gw_out, void* const* events, hipStream_t s, uint64_t* trace = nullptr) {
   const int D = L->d_model, F = L->d_ff, E = L->n_experts, k = L->top_k;
   const WsLayout W = layer_ws_layout(B, D, F, E, k);
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -85,21 +85,26 @@ int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
     if (events && events[i]) return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
     return hipSuccess;
   };
-  hipError_t e;
-  if ((e = rec(0)) != hipSuccess) return hip_status(e);
-  if ((e = launch_route(L->router_w, E, D, x_bf16, B, k, w, W, idx_out, gw_out, nullptr, s)) != hipSuccess)
-    return hip_status(e);
-  if ((e = rec(1)) != hipSuccess) return hip_status(e);
   const WeightRef g = wref(L->gate, L->gate_stride, L->gate_scale, L->gate_scale_stride);
   const WeightRef u = wref(L->up, L->up_stride, L->up_scale, L->up_scale_stride);
   const WeightRef d = wref(L->down, L->down_stride, L->down_scale, L->down_scale_stride);
-  if ((e = launch_gate_up(L->format, g, u, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
-  if ((e = rec(2)) != hipSuccess) return hip_status(e);
-  if ((e = launch_down(L->format, d, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
-  if ((e = rec(3)) != hipSuccess) return hip_status(e);
-  if ((e = launch_combine(D, B, k, w, W, y, residual, s)) != hipSuccess) return hip_status(e);
-  if ((e = rec(4)) != hipSuccess) return hip_status(e);
-  (void)ws_bytes;
+  hipError_t e;
+  if ((e = rec(0)) != hipSuccess) return hip_status(e);
+  const int grid = fused_grid_size();
+  int nx = xcd_count();
+  if (nx == 0) nx = probe_xcd_count(reinterpret_cast<uint32_t*>(w + W.topo), grid, s);
+  if (nx > 0 && fused_shape(L->format, B, k, D, F, grid, nx).ok) {
+    e = launch_fused_layer(L->format, L->router_w, x_bf16, g, u, d, E, D, F, k, B, w, W, y, residual, idx_out,
+                           gw_out, trace, s);
+    if (e != hipSuccess) return hip_status(e);
+  } else {
+    if ((e = launch_route(L->router_w, E, D, x_bf16, B, k, w, W, idx_out, gw_out, nullptr, s)) != hipSuccess)
+      return hip_status(e);
+    if ((e = launch_gate_up(L->format, g, u, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
+    if ((e = launch_down(L->format, d, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
+    if ((e = launch_combine(D, B, k, w, W, y, residual, s)) != hipSuccess) return hip_status(e);
+  }
+  if ((e = rec(1)) != hipSuccess) return hip_status(e);
   return MOE_OK;
 }
 
@@ -186,11 +191,22 @@ size_t moe_layer_workspace_bytes(int B, int D, int F, int E, int top_k) {
 }
 
 int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
-  if (!ws || ws_bytes < 64 * sizeof(uint32_t) || !aligned(ws, 256)) return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < 64 * sizeof(uint32_t) || !aligned(ws, 256) || ws_bytes % 4) return MOE_ERR_WORKSPACE;
   int st = arch_check();
   if (st != MOE_OK) return st;
-  // Counters sit at the start of every workspace layout.
-  return hip_status(launch_zero_u32(static_cast<uint32_t*>(ws), 64, (hipStream_t)stream));
+  hipStream_t s = (hipStream_t)stream;
+  // First use on this device: check the workgroup placement the single-launch
+  // layer relies on (synchronises the stream once), using the workspace as scratch.
+  if (xcd_count() == 0 && ws_bytes >= 4096 * sizeof(uint32_t))
+    probe_xcd_count(static_cast<uint32_t*>(ws), fused_grid_size(), s);
+  // Zero everything: counters, epoch and every tagged exchange word.
+  const size_t n = ws_bytes / 4;
+  for (size_t off = 0; off < n; off += (size_t)1 << 30) {
+    const size_t cnt = n - off < ((size_t)1 << 30) ? n - off : ((size_t)1 << 30);
+    hipError_t e = launch_zero_u32(static_cast<uint32_t*>(ws) + off, (int)cnt, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return MOE_OK;
 }
 
 int moe_layer_decode(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws, size_t ws_bytes,
@@ -207,7 +223,24 @@ int moe_layer_decode_profiled(const moe_layer_desc* L, const uint16_t* x_bf16, i
   const size_t need = layer_ws_layout(B, L->d_model, L->d_ff, L->n_experts, L->top_k).total;
   if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
   if ((st = arch_check()) != MOE_OK) return st;
-  return layer_impl(L, x_bf16, B, y, nullptr, ws, ws_bytes, idx_out, gw_out, events, (hipStream_t)stream);
+  return layer_impl(L, x_bf16, B, y, nullptr, ws, idx_out, gw_out, events, (hipStream_t)stream);
+}
+
+int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
+                            size_t ws_bytes, uint64_t* trace, int* trace_blocks, void* stream) {
+  int st = check_layer(L, B);
+  if (st != MOE_OK) return st;
+  if (!x_bf16 || !y || !trace_blocks) return MOE_ERR_ARG;
+  if (!aligned(x_bf16, 8) || !aligned(y, 16)) return MOE_ERR_ALIGN;
+  const size_t need = layer_ws_layout(B, L->d_model, L->d_ff, L->n_experts, L->top_k).total;
+  if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
+  if ((st = arch_check()) != MOE_OK) return st;
+  const int grid = fused_grid_size();
+  const int nx = xcd_count();
+  const bool fused = nx > 0 && fused_shape(L->format, B, L->top_k, L->d_model, L->d_ff, grid, nx).ok;
+  *trace_blocks = fused ? grid : 0;
+  if (!trace) return MOE_OK;  // size query
+  return layer_impl(L, x_bf16, B, y, nullptr, ws, nullptr, nullptr, nullptr, (hipStream_t)stream, trace);
 }
 
 size_t moe_stack_workspace_bytes(int B, int D, int F, int E, int top_k) {
@@ -241,7 +274,7 @@ int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* h_
   for (int l = 0; l < n_layers; ++l) {
     hipError_t e = launch_rmsnorm_bf16(cur, B, D, eps, xb, s);
     if (e != hipSuccess) return hip_status(e);
-    st = layer_impl(&layers[l], xb, B, h_out, cur, ws, layer_bytes, nullptr, nullptr, nullptr, s);
+    st = layer_impl(&layers[l], xb, B, h_out, cur, ws, nullptr, nullptr, nullptr, s);
     if (st != MOE_OK) return st;
     cur = h_out;
   }

@@ -129,7 +129,7 @@ static_assert(sizeof(ExpertGroup) == 80, "group record layout");
 
 // Byte offsets of the regions of a layer workspace (each 256-byte aligned).
 struct WsLayout {
-  size_t counters;  // uint32[64]: zeroed by moe_workspace_init, left zero by every call
+  size_t counters;  // uint32[64]: zeroed by moe_workspace_init (see kCtr* slots)
   size_t logits;    // fp64 [B][E]
   size_t idx;       // int32 [B][k]
   size_t gw;        // fp32 [B][k]
@@ -138,6 +138,11 @@ struct WsLayout {
   size_t xf;        // fp32 [B][D]: the activation widened from bfloat16
   size_t h;         // fp32 [B][k][F]: SiLU(gate) * up per (token, rank)
   size_t yp;        // fp32 [B][k][D]: down projection per (token, rank)
+  // Tagged exchange words of the single-launch layer (payload | epoch << 32):
+  size_t logit_tags;  // uint64 [B][E][2]: router logit, high and low halves
+  size_t h_tags;      // uint64 [B*k][F]: SiLU(gate) * up
+  size_t part_tags;   // uint64 [16][B][D]: per-XCD partial outputs (up to 16 XCDs)
+  size_t topo;        // uint32 [4096]: scratch of the placement check
   size_t total;
 };
 
@@ -155,12 +160,21 @@ inline WsLayout layer_ws_layout(int B, int D, int F, int E, int k) {
   L.xf = o;       o = align256(o + (size_t)B * D * sizeof(float));
   L.h = o;        o = align256(o + (size_t)B * k * F * sizeof(float));
   L.yp = o;       o = align256(o + (size_t)B * k * D * sizeof(float));
+  L.logit_tags = o; o = align256(o + (size_t)B * E * 2 * sizeof(uint64_t));
+  L.h_tags = o;     o = align256(o + (size_t)B * k * F * sizeof(uint64_t));
+  L.part_tags = o;  o = align256(o + (size_t)16 * B * D * sizeof(uint64_t));
+  L.topo = o;       o = align256(o + 4096 * sizeof(uint32_t));
   L.total = o;
   return L;
 }
 
 // Counter slots inside the counters region.
-enum : int { kCtrRoute = 0 };
+enum : int {
+  kCtrRoute = 0,     // arrivals in the stand-alone routing kernel (reset by its last workgroup)
+  kCtrEpoch = 16,    // number of the last completed single-launch call (tags of a call = epoch + 1)
+  kCtrXcdBase = 32,  // [16]: per-XCD arrival counters of the single-launch layer
+  kCtrTimeout = 63,  // set if a bounded wait gave up; stays set until the workspace is re-initialised
+};
 
 // ---------------------------------------------------------------- launchers
 // Each returns a hipError_t (hipSuccess on success).
@@ -196,5 +210,22 @@ hipError_t launch_quantize_int4(const uint8_t* mx, int64_t ngroups, int32_t* q, 
 hipError_t launch_validate_mxfp4(const uint8_t* blocks, int64_t n, int32_t* bad, hipStream_t s);
 
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
+
+// Single-launch layer (routing, gate/up, down and combine in one kernel).
+struct FusedShape {
+  bool ok;
+  int gu_units, dn_units, ups;
+};
+int fused_grid_size();
+FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx);
+// XCD count of the current device, measured once per device (the probe
+// synchronises `s`; scratch needs grid uint32).  xcd_count(): 0 not measured
+// yet, -1 placement unsuitable for the single-launch layer, else the count.
+int probe_xcd_count(uint32_t* scratch, int grid, hipStream_t s);
+int xcd_count();
+hipError_t launch_fused_layer(int fmt, const float* router_w, const uint16_t* x, const WeightRef& gate,
+                              const WeightRef& up, const WeightRef& down, int E, int D, int Fd, int k, int B,
+                              uint8_t* ws, const WsLayout& L, float* y, const float* residual, int32_t* idx_out,
+                              float* gw_out, uint64_t* trace, hipStream_t s);
 
 }  // namespace moe

@@ -84,8 +84,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ wr
       v[i] = id[i] < E ? __builtin_nontemporal_load(lt + id[i]) : 0.0;
     }
     uint32_t taken = 0;  // bit i: this lane's i-th logit already selected
-    double sel_v[kMaxTopK];
-    int sel_i[kMaxTopK];
+    double my_v = 0.0;   // lane r keeps the rank-r selection
+    int my_i = 0;
     for (int r = 0; r < k; ++r) {
       double bv = 0.0;
       int bi = 0x7FFFFFFF;
@@ -106,21 +106,20 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ wr
           bi = oi;
         }
       }
-      sel_v[r] = bv;
-      sel_i[r] = bi;
+      if (lane == r) {
+        my_v = bv;
+        my_i = bi;
+      }
       if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
     }
-    if (lane == 0) {
-      double ex[kMaxTopK];
-      double sum = 0.0;
-      for (int r = 0; r < k; ++r) {
-        ex[r] = exp(sel_v[r] - sel_v[0]);
-        sum += ex[r];
-      }
-      for (int r = 0; r < k; ++r) {
-        s_idx[t * k + r] = sel_i[r];
-        s_gw[t * k + r] = (float)(ex[r] / sum);
-      }
+    // Softmax over the selected logits (rank 0 is the largest), summed in rank order.
+    const double top = __shfl(my_v, 0, kWave);
+    const double ex = lane < k ? exp(my_v - top) : 0.0;
+    double sum = 0.0;
+    for (int r = 0; r < k; ++r) sum += __shfl(ex, r, kWave);
+    if (lane < k) {
+      s_idx[t * k + lane] = my_i;
+      s_gw[t * k + lane] = (float)(ex / sum);
     }
   }
   __syncthreads();
@@ -163,24 +162,21 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ wr
       const uint64_t used = __ballot(ex < E && mask != 0);
       if (ex < E && mask != 0) {
         const int pos = base + __popcll(used & ((1ull << lane) - 1ull));
-        ExpertGroup g;
-        g.expert = ex;
-        g.n = 0;
+        ExpertGroup* gr = &groups[pos];
+        gr->expert = ex;
+        gr->n = __popc(mask);
 #pragma unroll
         for (int t = 0; t < kMaxTok; ++t) {
-          g.tok[t] = 0;
-          g.slot[t] = 0;
-        }
-#pragma unroll
-        for (int t = 0; t < kMaxTok; ++t) {
+          const int p = __popc(mask & ((1u << t) - 1u));  // tokens ascending
           if ((mask >> t) & 1u) {
-            g.tok[g.n] = t;
-            g.slot[g.n] = slots[t];
-            ++g.n;
+            gr->tok[p] = t;
+            gr->slot[p] = slots[t];
           }
         }
-        g.pad[0] = g.pad[1] = 0;
-        groups[pos] = g;
+        for (int p = __popc(mask); p < kMaxTok; ++p) {
+          gr->tok[p] = 0;
+          gr->slot[p] = 0;
+        }
       }
       base += __popcll(used);
     }

@@ -134,6 +134,8 @@ class Layer:
         gw = torch.empty((B, self.k), dtype=torch.float32, device="cuda")
         moe.moe_layer_decode(self.desc, x, y, ws, idx, gw)
         torch.cuda.synchronize()
+        # counter slot 63 of the workspace flags a bounded wait that gave up
+        assert host(ws[63 * 4:64 * 4]).view(np.uint32)[0] == 0, "a wait in the layer kernel timed out"
         return host(y), host(idx), host(gw)
 
     def oracle(self, x_bf16: np.ndarray):

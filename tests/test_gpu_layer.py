@@ -43,6 +43,14 @@ def test_layer_small(fmt, B):
     _parity(L, xb, f"{fmt} small B={B}")
 
 
+def test_layer_multi_launch_fallback_shape():
+    # d_model 8192 has more MXFP4 blocks per row than the single-launch
+    # kernel keeps per lane, so the layer runs as separate launches.
+    L = layer("mxfp4", 16, 8192, 256, 6, seed=13)
+    for B in (1, 8):
+        _parity(L, synth.token_bf16(700 + B, B, 8192), f"fallback B={B}")
+
+
 def test_layer_small_ragged_topk_and_experts():
     L = layer("mxfp4", 10, 96, 64, 3, seed=12)
     for B in (1, 4, 8):
@@ -64,8 +72,16 @@ def test_layer_full_other_formats(fmt, B):
     print(f"{fmt} layer B={B}: max rel-inf err {err:.3e}")
 
 
+def _single_launch(L, B):
+    import quantized_moe_decode_route_amd as moe
+    x = torch.zeros((B, L.D), dtype=torch.int16, device="cuda")
+    y = torch.empty((B, L.D), dtype=torch.float32, device="cuda")
+    return moe.moe_layer_decode_traced(L.desc, x, y, L.workspace(B)) is not None
+
+
 def test_layer_invariants_full_shape():
     L = layer("mxfp4", 256, 4096, 2048)
+    assert _single_launch(L, 1) and _single_launch(L, 8), "full layer shape should run as one launch"
     x8 = synth.token_bf16(3000, 8, 4096)
     ws = L.workspace(8)
     y8a, i8a, _ = L.run(x8, ws)
