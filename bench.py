@@ -36,24 +36,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def build_layers(n_layers: int, seed: int):
+def build_layers(n_layers: int, seed: int, down_layout: str = "tile256"):
+    """MXFP4 layers filled on the GPU from the seeded generator.  With
+    down_layout "tile256" each expert's down projection is permuted once into
+    the 256-column tiled layout (moe_tile_weights), as a loader would."""
     import torch
 
     import quantized_moe_decode_route_amd as moe
     import synth
     stream = torch.cuda.current_stream().cuda_stream
     layers = []
+    tmp = torch.empty(E * MX_MAT, dtype=torch.uint8, device="cuda") if down_layout == "tile256" else None
     for l in range(n_layers):
         mats = []
         for proj in (synth.PROJ_GATE, synth.PROJ_UP, synth.PROJ_DOWN):
             buf = torch.empty(E * MX_MAT, dtype=torch.uint8, device="cuda")
-            synth.gpu_fill("mxfp4", buf.data_ptr(), seed, l, 0, E, proj, F * D // 32, stream)
+            if proj == synth.PROJ_DOWN and tmp is not None:
+                synth.gpu_fill("mxfp4", tmp.data_ptr(), seed, l, 0, E, proj, F * D // 32, stream)
+                for e in range(E):
+                    moe.moe_tile_weights("mxfp4", tmp.data_ptr() + e * MX_MAT, D, F, buf.data_ptr() + e * MX_MAT)
+            else:
+                synth.gpu_fill("mxfp4", buf.data_ptr(), seed, l, 0, E, proj, F * D // 32, stream)
             mats.append(buf)
         router = torch.from_numpy(synth.router_weights(seed, l, E, D)).to("cuda")
         desc = moe.make_layer_desc("mxfp4", router, mats[0], mats[1], mats[2], E, D, F, TOPK,
-                                   MX_MAT, MX_MAT, MX_MAT)
+                                   MX_MAT, MX_MAT, MX_MAT, down_layout=down_layout)
         layers.append((desc, mats, router))
     torch.cuda.synchronize()
+    del tmp
     return layers
 
 
@@ -137,6 +147,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0x5EED + 1)
     ap.add_argument("--cpu-tokens", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--down-layout", choices=("tile256", "rows"), default="tile256",
+                    help="layout of the down projections (blocks permuted once at load time)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this decode path "
@@ -150,7 +162,7 @@ def main():
     torch.cuda.set_device(0)
     moe.moe_device_check()
     log(f"building {args.layers} MXFP4 layers ({args.layers * 3 * E * MX_MAT / 1e9:.1f} GB) ...")
-    layers = build_layers(args.layers, args.seed)
+    layers = build_layers(args.layers, args.seed, args.down_layout)
     n_tok = args.warmup + args.steps
     x1 = [torch.from_numpy(synth.token_bf16(10000 + i, 1, D).view(np.int16)).to("cuda") for i in range(n_tok)]
     x8 = [torch.from_numpy(synth.token_bf16(20000 + i, 8, D).view(np.int16)).to("cuda") for i in range(n_tok)]
@@ -189,7 +201,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "moe_layer_decode_mxfp4_b1", "experts": E, "top_k": TOPK, "d_model": D,
                    "d_ff": F, "tokens_per_step": 1, "weight_format": "mxfp4",
-                   "layer_instances_rotated": args.layers},
+                   "down_layout": args.down_layout, "layer_instances_rotated": args.layers},
         "pct_hbm_peak": round(100 * gbs1 / HBM_PEAK_GBS, 2),
         "tokens_per_s_layer": round(1e3 / ms1, 1),
         "bytes_per_step": bytes1,

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 enum moe_status {
   MOE_OK = 0,
@@ -58,6 +58,20 @@ enum moe_status {
 };
 
 enum moe_format { MOE_FMT_MXFP4 = 0, MOE_FMT_Q2K = 1, MOE_FMT_INT4G32 = 2 };
+
+/* Order of the quantized blocks of a weight matrix [N][K] in memory.  The
+ * blocks themselves (and INT4 words and scales) are unchanged; only their
+ * order differs.
+ *   MOE_LAYOUT_ROWS     row-major, as the formats are published: row n holds
+ *                       its K/32 (K/256 for Q2_K) blocks in order.
+ *   MOE_LAYOUT_TILE256  K is cut into K/256 column tiles of 256 weights and
+ *                       the tiles are stored one after the other, each
+ *                       row-major: the matrix is stored as the row-major
+ *                       [(K/256) * N][256] matrix whose row c*N + n holds
+ *                       columns 256c .. 256c+255 of row n.  A decode kernel
+ *                       that splits K over the chip's XCDs then reads one
+ *                       contiguous region per XCD.  K % 256 == 0. */
+enum moe_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILE256 = 1 };
 
 #define MOE_MAX_TOKENS 8   /* B: one token plus up to 7 speculative drafts */
 #define MOE_MAX_TOPK 8
@@ -136,14 +150,17 @@ typedef struct moe_layer_desc {
   const uint16_t* up_scale;
   const uint16_t* down_scale;
   int64_t gate_scale_stride, up_scale_stride, down_scale_stride;
+  int down_layout;   /* enum moe_layout of every expert's down projection
+                      * (and of its INT4 scales); gate and up are row-major */
 } moe_layer_desc;
 
 /* Workspace for moe_layer_decode with up to B tokens (256-byte aligned). */
 size_t moe_layer_workspace_bytes(int B, int D, int F, int E, int top_k);
 /* Prepare a fresh workspace (zeroes its counters); enqueued on `stream`. */
 int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
-/* x bfloat16 bits [B][D]; y fp32 [B][D] (overwritten).  idx_out int32
- * [B][top_k] and gw_out fp32 [B][top_k] receive the routing if not NULL. */
+/* x bfloat16 bits [B][D] (16-byte aligned); y fp32 [B][D] (overwritten,
+ * 16-byte aligned).  idx_out int32 [B][top_k] and gw_out fp32 [B][top_k]
+ * receive the routing if not NULL. */
 int moe_layer_decode(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
                      size_t ws_bytes, int32_t* idx_out, float* gw_out, void* stream);
 /* Same, recording two hipEvent_t (passed as void*) on `stream` right before
@@ -155,11 +172,14 @@ int moe_layer_decode_profiled(const moe_layer_desc* L, const uint16_t* x_bf16, i
 /* Diagnostic: the same layer decode with per-phase wall-clock stamps.  With
  * trace == NULL only *trace_blocks is set: the number of workgroups of the
  * single-launch kernel (0 if the shape runs as separate launches, which are
- * not traced).  Otherwise trace (device, uint64 [*trace_blocks][10]) receives,
- * per workgroup, the 100 MHz wall clock at: start, own router logits
- * published, top-k and grouping done, gate/up done, h slice gathered, down
- * done, partial outputs published, end; then the workgroup's XCD and the
- * raw value of its XCD arrival counter. */
+ * not traced).  Otherwise trace (device, uint64 [*trace_blocks][MOE_TRACE_FIELDS], zeroed by
+ * the caller) receives, per workgroup, in slots 0..10 the 100 MHz wall clock
+ * at: start, own router logits published, activations staged, all logits
+ * gathered (wave 0), top-k done, grouping done, gate/up done, h slice
+ * gathered, down done, partial outputs published, end; slots 11..13 are
+ * reserved; slot 14 is the workgroup's XCD and slot 15 the raw value of its
+ * XCD arrival counter. */
+#define MOE_TRACE_FIELDS 16 /* uint64 per workgroup in moe_layer_decode_traced */
 int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
                             size_t ws_bytes, uint64_t* trace, int* trace_blocks, void* stream);
 
@@ -191,6 +211,16 @@ int moe_rmsnorm_bf16(const float* h, int B, int D, double eps, uint16_t* x_out, 
  */
 int quantize_fp4_to_int4g32(const uint8_t* mxfp4, int N, int K, int32_t* q_out, uint16_t* scale_out,
                             void* stream);
+
+/* ------------------------------------------------------------------ layout
+ * Copies a weight matrix [N][K] of `format` from MOE_LAYOUT_ROWS (src) to
+ * MOE_LAYOUT_TILE256 (dst): a permutation of whole blocks, done once when
+ * the weights are loaded.  For INT4G32, src/dst are the int32 code arrays
+ * and src_scale/dst_scale the bfloat16 scale arrays (else NULL).  K % 256 ==
+ * 0; src and dst do not overlap; pointers 4-byte aligned (INT4 codes 16).
+ * Returns MOE_ERR_SHAPE / _ALIGN / _ARG on bad arguments, before any work. */
+int moe_tile_weights(int format, const void* src, const uint16_t* src_scale, int N, int K, void* dst,
+                     uint16_t* dst_scale, void* stream);
 
 /* Count MXFP4 blocks whose exponent byte is 0xFF (scale +inf: infinity times
  * a zero code is NaN, which the ds4 notes treat as an error for E8M0 scales).

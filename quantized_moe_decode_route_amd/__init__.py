@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(PKG_DIR, "libmoedecode.so")
 MOE_OK = 0
 MOE_FMT_MXFP4, MOE_FMT_Q2K, MOE_FMT_INT4G32 = 0, 1, 2
 FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2k": MOE_FMT_Q2K, "int4g32": MOE_FMT_INT4G32}
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE256 = 0, 1
+LAYOUTS = {"rows": MOE_LAYOUT_ROWS, "tile256": MOE_LAYOUT_TILE256}
 MOE_MAX_TOKENS = 8
 MOE_MAX_TOPK = 8
 
@@ -27,7 +29,7 @@ EXPORTS = (
     "moe_layer_workspace_bytes", "moe_workspace_init", "moe_layer_decode", "moe_layer_decode_profiled",
     "moe_layer_decode_traced",
     "moe_stack_workspace_bytes", "moe_stack_decode", "moe_rmsnorm_bf16",
-    "quantize_fp4_to_int4g32", "moe_validate_mxfp4",
+    "quantize_fp4_to_int4g32", "moe_validate_mxfp4", "moe_tile_weights",
 )
 
 
@@ -50,6 +52,7 @@ class moe_layer_desc(ctypes.Structure):
         ("gate_scale", ctypes.c_void_p), ("up_scale", ctypes.c_void_p), ("down_scale", ctypes.c_void_p),
         ("gate_scale_stride", ctypes.c_int64), ("up_scale_stride", ctypes.c_int64),
         ("down_scale_stride", ctypes.c_int64),
+        ("down_layout", ctypes.c_int),
     ]
 
 
@@ -86,6 +89,7 @@ def lib() -> ctypes.CDLL:
             "moe_rmsnorm_bf16": (_i, [_vp, _i, _i, _d, _vp, _vp]),
             "quantize_fp4_to_int4g32": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
             "moe_validate_mxfp4": (_i, [_vp, _i64, _vp, _vp]),
+            "moe_tile_weights": (_i, [_i, _vp, _vp, _i, _i, _vp, _vp, _vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -175,8 +179,9 @@ def moe_workspace_init(ws, stream=None) -> None:
 def make_layer_desc(fmt: str, router_w, gate, up, down, n_experts: int, d_model: int, d_ff: int, top_k: int,
                     gate_stride: int, up_stride: int, down_stride: int, gate_scale=None, up_scale=None,
                     down_scale=None, gate_scale_stride: int = 0, up_scale_stride: int = 0,
-                    down_scale_stride: int = 0) -> moe_layer_desc:
-    """Fill the C descriptor; tensors (or raw device addresses) must outlive its use."""
+                    down_scale_stride: int = 0, down_layout: str = "rows") -> moe_layer_desc:
+    """Fill the C descriptor; tensors (or raw device addresses) must outlive its use.
+    ``down_layout``: "rows" (as published) or "tile256" (see moe_tile_weights)."""
     d = moe_layer_desc()
     d.format = FORMATS[fmt]
     d.n_experts, d.d_model, d.d_ff, d.top_k = n_experts, d_model, d_ff, top_k
@@ -185,6 +190,7 @@ def make_layer_desc(fmt: str, router_w, gate, up, down, n_experts: int, d_model:
     d.gate_stride, d.up_stride, d.down_stride = gate_stride, up_stride, down_stride
     d.gate_scale, d.up_scale, d.down_scale = _ptr(gate_scale), _ptr(up_scale), _ptr(down_scale)
     d.gate_scale_stride, d.up_scale_stride, d.down_scale_stride = gate_scale_stride, up_scale_stride, down_scale_stride
+    d.down_layout = LAYOUTS[down_layout]
     return d
 
 
@@ -206,10 +212,13 @@ def moe_layer_decode_profiled(desc: moe_layer_desc, x_bf16, y, ws, events, idx_o
                                            _stream(stream)))
 
 
+TRACE_FIELDS = 16  # per workgroup: 14 time-stamp slots, XCD, XCD arrival counter
+
+
 def moe_layer_decode_traced(desc: moe_layer_desc, x_bf16, y, ws, stream=None):
-    """Run the layer and return per-workgroup records (int64 [blocks, 10]: eight
-    100 MHz phase stamps, the XCD, the XCD arrival counter) as a device
-    tensor, or None if the shape is not traced."""
+    """Run the layer and return per-workgroup records (int64 [blocks, 16]:
+    14 slots of 100 MHz phase stamps (11 used), the XCD, the XCD arrival
+    counter) as a device tensor, or None if the shape is not traced."""
     import torch
     B = x_bf16.shape[0]
     nb = ctypes.c_int(0)
@@ -219,7 +228,7 @@ def moe_layer_decode_traced(desc: moe_layer_desc, x_bf16, y, ws, stream=None):
     if nb.value == 0:
         moe_layer_decode(desc, x_bf16, y, ws, stream=stream)
         return None
-    tr = torch.zeros((nb.value, 10), dtype=torch.int64, device=x_bf16.device)
+    tr = torch.zeros((nb.value, TRACE_FIELDS), dtype=torch.int64, device=x_bf16.device)
     _check("moe_layer_decode_traced",
            lib().moe_layer_decode_traced(ctypes.byref(desc), _ptr(x_bf16), B, _ptr(y), _ptr(ws),
                                          ws.numel() * ws.element_size(), _ptr(tr), ctypes.byref(nb),
@@ -247,6 +256,13 @@ def moe_rmsnorm_bf16(h, x_out, eps: float = 1e-6, stream=None) -> None:
 def quantize_fp4_to_int4g32(mxfp4, N: int, K: int, q_out, scale_out, stream=None) -> None:
     _check("quantize_fp4_to_int4g32",
            lib().quantize_fp4_to_int4g32(_ptr(mxfp4), N, K, _ptr(q_out), _ptr(scale_out), _stream(stream)))
+
+
+def moe_tile_weights(fmt: str, src, N: int, K: int, dst, src_scale=None, dst_scale=None, stream=None) -> None:
+    """Row-major [N][K] weights of ``fmt`` -> the 256-column tiled layout (a block permutation)."""
+    _check("moe_tile_weights",
+           lib().moe_tile_weights(FORMATS[fmt], _ptr(src), _ptr(src_scale), N, K, _ptr(dst), _ptr(dst_scale),
+                                  _stream(stream)))
 
 
 def moe_validate_mxfp4(blocks, n_blocks: int, bad_count_dev, stream=None) -> None:

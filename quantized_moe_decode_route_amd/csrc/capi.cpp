@@ -59,6 +59,8 @@ int check_layer(const moe_layer_desc* L, int B) {
   const uintptr_t wa = L->format == MOE_FMT_INT4G32 ? 16 : 4;
   if (!aligned(L->gate, wa) || !aligned(L->up, wa) || !aligned(L->down, wa)) return MOE_ERR_ALIGN;
   if (L->gate_stride % wa || L->up_stride % wa || L->down_stride % wa) return MOE_ERR_ALIGN;
+  if (L->down_layout != MOE_LAYOUT_ROWS && L->down_layout != MOE_LAYOUT_TILE256) return MOE_ERR_ARG;
+  if (L->down_layout == MOE_LAYOUT_TILE256 && L->d_ff % kTileCols) return MOE_ERR_SHAPE;
   if (L->format == MOE_FMT_INT4G32) {
     if (!L->gate_scale || !L->up_scale || !L->down_scale) return MOE_ERR_ARG;
     if (!aligned(L->gate_scale, 2) || !aligned(L->up_scale, 2) || !aligned(L->down_scale, 2)) return MOE_ERR_ALIGN;
@@ -67,12 +69,13 @@ int check_layer(const moe_layer_desc* L, int B) {
   return MOE_OK;
 }
 
-WeightRef wref(const void* base, int64_t stride, const uint16_t* scale, int64_t scale_stride) {
+WeightRef wref(const void* base, int64_t stride, const uint16_t* scale, int64_t scale_stride, int layout) {
   WeightRef w;
   w.base = static_cast<const uint8_t*>(base);
   w.stride = stride;
   w.scale = scale;
   w.scale_stride = scale_stride;
+  w.tiled = layout == MOE_LAYOUT_TILE256 ? 1 : 0;
   return w;
 }
 
@@ -85,9 +88,9 @@ int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
     if (events && events[i]) return hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
     return hipSuccess;
   };
-  const WeightRef g = wref(L->gate, L->gate_stride, L->gate_scale, L->gate_scale_stride);
-  const WeightRef u = wref(L->up, L->up_stride, L->up_scale, L->up_scale_stride);
-  const WeightRef d = wref(L->down, L->down_stride, L->down_scale, L->down_scale_stride);
+  const WeightRef g = wref(L->gate, L->gate_stride, L->gate_scale, L->gate_scale_stride, MOE_LAYOUT_ROWS);
+  const WeightRef u = wref(L->up, L->up_stride, L->up_scale, L->up_scale_stride, MOE_LAYOUT_ROWS);
+  const WeightRef d = wref(L->down, L->down_stride, L->down_scale, L->down_scale_stride, L->down_layout);
   hipError_t e;
   if ((e = rec(0)) != hipSuccess) return hip_status(e);
   const int grid = fused_grid_size();
@@ -219,7 +222,7 @@ int moe_layer_decode_profiled(const moe_layer_desc* L, const uint16_t* x_bf16, i
   int st = check_layer(L, B);
   if (st != MOE_OK) return st;
   if (!x_bf16 || !y) return MOE_ERR_ARG;
-  if (!aligned(x_bf16, 8) || !aligned(y, 16)) return MOE_ERR_ALIGN;
+  if (!aligned(x_bf16, 16) || !aligned(y, 16)) return MOE_ERR_ALIGN;
   const size_t need = layer_ws_layout(B, L->d_model, L->d_ff, L->n_experts, L->top_k).total;
   if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
   if ((st = arch_check()) != MOE_OK) return st;
@@ -231,7 +234,7 @@ int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int
   int st = check_layer(L, B);
   if (st != MOE_OK) return st;
   if (!x_bf16 || !y || !trace_blocks) return MOE_ERR_ARG;
-  if (!aligned(x_bf16, 8) || !aligned(y, 16)) return MOE_ERR_ALIGN;
+  if (!aligned(x_bf16, 16) || !aligned(y, 16)) return MOE_ERR_ALIGN;
   const size_t need = layer_ws_layout(B, L->d_model, L->d_ff, L->n_experts, L->top_k).total;
   if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
   if ((st = arch_check()) != MOE_OK) return st;
@@ -296,6 +299,28 @@ int quantize_fp4_to_int4g32(const uint8_t* mxfp4, int N, int K, int32_t* q_out, 
   int st = arch_check();
   if (st != MOE_OK) return st;
   return hip_status(launch_quantize_int4(mxfp4, (int64_t)N * (K / 32), q_out, scale_out, (hipStream_t)stream));
+}
+
+int moe_tile_weights(int format, const void* src, const uint16_t* src_scale, int N, int K, void* dst,
+                     uint16_t* dst_scale, void* stream) {
+  if (format < MOE_FMT_MXFP4 || format > MOE_FMT_INT4G32) return MOE_ERR_ARG;
+  if (!src || !dst || N <= 0 || K <= 0) return MOE_ERR_ARG;
+  if (K % kTileCols) return MOE_ERR_SHAPE;
+  const bool int4 = format == MOE_FMT_INT4G32;
+  if (int4 && (!src_scale || !dst_scale)) return MOE_ERR_ARG;
+  if (!int4 && (src_scale || dst_scale)) return MOE_ERR_ARG;
+  if (!aligned(src, int4 ? 16 : 4) || !aligned(dst, int4 ? 16 : 4)) return MOE_ERR_ALIGN;
+  if (int4 && (!aligned(src_scale, 2) || !aligned(dst_scale, 2))) return MOE_ERR_ALIGN;
+  int st = arch_check();
+  if (st != MOE_OK) return st;
+  const int tiles = K / kTileCols;
+  hipStream_t s = (hipStream_t)stream;
+  // Bytes of one row of one tile: 8 MXFP4 blocks, 1 Q2_K block, or 32 INT4
+  // code words (+ 8 bfloat16 scales).
+  const int tile_bytes = format == MOE_FMT_MXFP4 ? 8 * 17 : format == MOE_FMT_Q2K ? 84 : 128;
+  hipError_t e = launch_tile_rows(src, dst, N, tiles, tile_bytes / 4, 4, s);
+  if (e == hipSuccess && int4) e = launch_tile_rows(src_scale, dst_scale, N, tiles, kTileCols / 32, 2, s);
+  return hip_status(e);
 }
 
 int moe_validate_mxfp4(const uint8_t* blocks, int64_t n_blocks, int32_t* bad_count_dev, void* stream) {

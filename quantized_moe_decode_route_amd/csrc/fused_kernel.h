@@ -1,0 +1,781 @@
+// One MoE layer in a single launch: one 512-thread workgroup per compute
+// unit, no grid barriers and no memory fences on the hot path.
+//
+// Workgroups exchange results through tagged 64-bit words: a 32-bit payload
+// plus the call's epoch number.  A consumer spins on the words it needs until
+// every tag equals the current epoch, so each dependency waits exactly for
+// the data it consumes.  All exchanges use agent-coherent 64-bit accesses
+// (workgroup-scope stores are not reliably seen by other compute units of the
+// same XCD while the kernel runs).  A workgroup learns its XCD from the
+// XCC_ID hardware register and its index inside the XCD from an L2-local
+// counter: with one workgroup per compute unit (the LDS footprint allows no
+// more), every XCD holds exactly grid/NX of them, whatever order the
+// dispatcher used.
+//
+//  1. Routing.  Workgroup g computes expert g's router logits for every token
+//     (fp64) and publishes them device-wide.  Every workgroup gathers all
+//     logits and derives, identically, each token's top-k (largest first, ties
+//     to the lower index), the softmax weights and the grouping of
+//     (token, rank) pairs by expert.
+//  2. Gate/up.  XCD x owns the d_ff slice [x*F/NX, (x+1)*F/NX): its workgroups
+//     compute h = SiLU(gate.x) * (up.x) for those rows of every selected
+//     expert, keeping the next experts' blocks in flight, and publish h.
+//  3. Down.  XCD x requests its first experts' down blocks, gathers its own h
+//     slice, multiplies every down row's slice-x columns by it (partial sums
+//     over d_ff), combines the k ranks of each token in rank order, and
+//     publishes the partial outputs device-wide; the output rows are then
+//     finished by summing the NX partials in XCD order.
+//
+// A token's arithmetic does not depend on the other tokens in the call (same
+// lane mapping, same reduction trees), so B=8 rows equal B=1 results bit for
+// bit.  Every wait is bounded (about 0.5 s); on timeout a flag is raised in
+// the workspace and the kernel runs to completion.
+#pragma once
+
+#include "units.h"
+
+namespace moe {
+namespace fused {
+
+
+constexpr int kW = 8;     // waves per workgroup
+constexpr int kMaxNX = 16; // XCDs supported
+constexpr int kTracePoints = MOE_TRACE_FIELDS;  // 14 time-stamp slots, then the XCD and the raw XCD counter
+static_assert(kTracePoints == 16, "trace record layout");
+constexpr uint64_t kSpinTicks = 50000000ull;  // 0.5 s of the 100 MHz wall clock
+
+// ---------------------------------------------------------------- tagged exchange
+
+__device__ __forceinline__ uint64_t tagged(uint32_t payload, uint32_t tag) {
+  return ((uint64_t)tag << 32) | payload;
+}
+__device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
+__device__ __forceinline__ uint32_t payload_of(uint64_t w) { return (uint32_t)w; }
+
+// device-wide (agent-coherent)
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// First read of a word written by a workgroup of the same XCD: may be served
+// by the XCD's L2 (which that workgroup's agent-coherent store went through)
+// or by a line this compute unit cached earlier in the call.  A stale value
+// is recognised by its tag and read again with ld_dev.
+__device__ __forceinline__ uint64_t ld_xcd(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// ---------------------------------------------------------------- DPP reductions
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                                               false));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int v, int old) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Sum over the wave in a fixed tree; the total lands in lane 63.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0xB1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);        // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);       // row_half_mirror
+  v += dpp_f<0x140>(v);       // row_mirror
+  v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
+// Sum over aligned groups of G lanes (G = 1, 2, 4, 8 or 16); every lane of a
+// group ends with the group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  if (G >= 2) v += dpp_f<0xB1>(v);
+  if (G >= 4) v += dpp_f<0x4E>(v);
+  if (G >= 8) v += dpp_f<0x141>(v);
+  if (G >= 16) v += dpp_f<0x140>(v);
+  return v;
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_d(double v) {
+  const int lo = dpp_i<CTRL, ROW_MASK>(__double2loint(v), 0);
+  const int hi = dpp_i<CTRL, ROW_MASK>(__double2hiint(v), 0);
+  return __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ double wave_sum_dpp_f64(double v) {
+  v += dpp_d<0xB1>(v);
+  v += dpp_d<0x4E>(v);
+  v += dpp_d<0x141>(v);
+  v += dpp_d<0x140>(v);
+  v += dpp_d<0x142, 0xA>(v);
+  v += dpp_d<0x143, 0xC>(v);
+  return v;
+}
+
+// (value, index) with "better" = larger value, then lower index.
+__device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ void argmax_step(double& v, int& i) {
+  // Lanes without a source read (-inf, INT_MAX), which never wins.
+  const int lo = dpp_i<CTRL, ROW_MASK>(__double2loint(v), 0);
+  const int hi = dpp_i<CTRL, ROW_MASK>(__double2hiint(v), (int)0xFFF00000);
+  const int oi = dpp_i<CTRL, ROW_MASK>(i, 0x7FFFFFFF);
+  const double ov = __hiloint2double(hi, lo);
+  if (better(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Wave-wide best (value, index), returned uniformly to all lanes.
+__device__ __forceinline__ void wave_argmax(double& v, int& i) {
+  argmax_step<0xB1>(v, i);
+  argmax_step<0x4E>(v, i);
+  argmax_step<0x141>(v, i);
+  argmax_step<0x140>(v, i);
+  argmax_step<0x142, 0xA>(v, i);
+  argmax_step<0x143, 0xC>(v, i);
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), 63);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), 63);
+  i = __builtin_amdgcn_readlane(i, 63);
+  v = __hiloint2double(hi, lo);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+struct FusedArgs {
+  const float* router_w;
+  const uint16_t* x;  // bf16 bits [B][D]
+  WeightRef gate, up, down;
+  uint8_t* ws;
+  WsLayout L;
+  float* y;
+  const float* residual;
+  int32_t* idx_out;
+  float* gw_out;
+  uint64_t* trace;
+  int E, D, Fd, k, B;
+  int nx;  // XCDs (the grid holds grid/nx workgroups on each)
+};
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID bits 3:0
+}
+
+__device__ __forceinline__ void stamp(const FusedArgs& a, int point) {
+  if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints + point] = wall_clock64();
+}
+
+// Marks every dword of a ring slot as used here, on every path: the wave
+// waits for the slot's loads at this point, so the compiler knows that no
+// load into the slot is pending when the slot is refilled.
+template <class T>
+__device__ __forceinline__ void consume(const T& raw) {
+  static_assert(sizeof(T) % 4 == 0, "ring slots are dwords");
+  const uint32_t* d = reinterpret_cast<const uint32_t*>(&raw);
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"v"(d[i]));
+}
+
+// Waits (bounded) until every valid word i < N carries `tag`: v[i] holds the
+// first read of word addr(i) and receives the current one.  Each pass
+// re-reads all stale words together, so one pass costs one memory round trip
+// however many words were stale.
+template <int N, class Addr>
+__device__ __forceinline__ void await_tags(Addr addr, uint64_t (&v)[N], const bool (&valid)[N], uint32_t tag,
+                                           uint64_t t0, int* timeout) {
+  static_assert(N <= 32, "stale words are tracked in a 32-bit mask");
+#pragma nounroll
+  for (;;) {
+    uint32_t stale = 0u;
+#pragma unroll
+    for (int i = 0; i < N; ++i) stale |= (valid[i] && tag_of(v[i]) != tag) ? (1u << i) : 0u;
+    if (stale == 0u) return;
+    if (wall_clock64() - t0 > kSpinTicks) {
+      *timeout = 1;
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    uint64_t again[N];  // every word is re-read (all requests first); stale ones take the new value
+#pragma unroll
+    for (int i = 0; i < N; ++i) again[i] = ld_dev(addr(i));
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = ((stale >> i) & 1u) ? again[i] : v[i];
+  }
+}
+
+// LDS shared by the phases (activations during gate/up; h slices and row
+// partials during down).
+constexpr int kLdsBytes = 128 * 1024;
+// Experts whose weights a wave has in flight or in use: the loads for expert
+// uu + R - 1 are issued before expert uu is computed.  The rings are indexed
+// with compile-time constants only (no register copies, which would make the
+// wave wait for every load in flight), and every load is issued
+// unconditionally (past the last expert, one cached unit for the whole wave)
+// so the number of loads between a load and its use is fixed.
+constexpr int kRingGU = 4;
+constexpr int kRingDN = 6;
+constexpr int kSpinBatch = 12;  // tagged words a thread reads before its first wait
+
+template <class F, int MAXU_GU, int MAXU_DN, int UPS>
+__global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a) {
+  constexpr int kCh = F::kXDw / 4;  // 16-byte chunks of one unit's staged activations
+  const int G = gridDim.x;
+  const int g = blockIdx.x;
+  const int w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int B = a.B, k = a.k, E = a.E, D = a.D, Fd = a.Fd;
+  const int S = B * k;  // (token, rank) slots
+  stamp(a, 0);
+  uint32_t* ctr = reinterpret_cast<uint32_t*>(a.ws + a.L.counters);
+  uint32_t tag = ctr[kCtrEpoch] + 1u;  // this call's epoch
+  if (tag == 0u) tag = 1u;              // tags start at 1 (the workspace starts zeroed)
+
+  __shared__ int32_t s_idx[kMaxSlots];
+  __shared__ float s_gw[kMaxSlots];
+  __shared__ ExpertGroup s_grp[kMaxSlots];
+  __shared__ uint32_t s_mask[MOE_MAX_EXPERTS];  // per expert: tokens that picked it and at which rank
+  __shared__ double s_part[kW][kMaxTok];
+  __shared__ float s_hv[kW][kMaxSlots];  // a wave's h values for its current row, per slot
+  __shared__ int s_U;
+  __shared__ int s_timeout;
+  __shared__ int s_jx;
+  __shared__ __align__(16) uint8_t s_buf[kLdsBytes];
+
+  const int NX = a.nx;
+  const int xcd = (int)xcc_id();
+  const int GX = G / NX;  // workgroups per XCD
+  // Index inside the XCD: every call adds exactly GX to each XCD's counter.
+  // The result is first used after the router logits, so its latency hides
+  // behind them.
+  uint32_t xcd_arrival = 0;
+  if (threadIdx.x == 0) {
+    s_timeout = 0;
+    xcd_arrival = __hip_atomic_fetch_add(ctr + kCtrXcdBase + xcd, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  for (int i = threadIdx.x; i < MOE_MAX_EXPERTS; i += blockDim.x) s_mask[i] = 0u;
+
+  // Activations for gate/up: requested now, staged after the router logits
+  // (registers for one token; LDS [t][chunk][unit] for several, so lanes read
+  // consecutive chunks).  B * units <= 2 * blockDim for every shape this
+  // kernel accepts.
+  const int UG = F::units(D);
+  uint32_t xraw[2][F::kXRaw];
+  if (B == 1) {
+#pragma unroll
+    for (int j = 0; j < MAXU_GU && j < 2; ++j) {
+      const int u = lane + kWave * j;
+      if (u < UG) F::load_x(a.x, u, xraw[j]);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = threadIdx.x + q * kW * kWave;
+      if (i < B * UG) F::load_x(a.x + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);
+    }
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- 1. routing
+  uint64_t* lg = reinterpret_cast<uint64_t*>(a.ws + a.L.logit_tags);  // [B][E][2]: high, low halves
+  for (int e = g; e < E; e += G) {
+    const float* row = a.router_w + (int64_t)e * D;
+    double acc[kMaxTok];
+#pragma unroll
+    for (int t = 0; t < kMaxTok; ++t) acc[t] = 0.0;
+    for (int c = 8 * threadIdx.x; c < D; c += 8 * kW * kWave) {
+      const float4 w0 = *reinterpret_cast<const float4*>(row + c);
+      const float4 w1 = *reinterpret_cast<const float4*>(row + c + 4);
+      uint4 xall[kMaxTok];  // every token's activations requested before the first use
+#pragma unroll
+      for (int t = 0; t < kMaxTok; ++t) xall[t] = *reinterpret_cast<const uint4*>(a.x + (int64_t)min(t, B - 1) * D + c);
+#pragma unroll
+      for (int t = 0; t < kMaxTok; ++t) {
+        if (t < B) {
+          const uint4 xv = xall[t];
+          acc[t] = __builtin_fma((double)w0.x, (double)bf16_to_f32(xv.x & 0xFFFFu), acc[t]);
+          acc[t] = __builtin_fma((double)w0.y, (double)bf16_to_f32(xv.x >> 16), acc[t]);
+          acc[t] = __builtin_fma((double)w0.z, (double)bf16_to_f32(xv.y & 0xFFFFu), acc[t]);
+          acc[t] = __builtin_fma((double)w0.w, (double)bf16_to_f32(xv.y >> 16), acc[t]);
+          acc[t] = __builtin_fma((double)w1.x, (double)bf16_to_f32(xv.z & 0xFFFFu), acc[t]);
+          acc[t] = __builtin_fma((double)w1.y, (double)bf16_to_f32(xv.z >> 16), acc[t]);
+          acc[t] = __builtin_fma((double)w1.z, (double)bf16_to_f32(xv.w & 0xFFFFu), acc[t]);
+          acc[t] = __builtin_fma((double)w1.w, (double)bf16_to_f32(xv.w >> 16), acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kMaxTok; ++t) {
+      if (t < B) {
+        const double v = wave_sum_dpp_f64(acc[t]);
+        if (lane == 63) s_part[w][t] = v;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < B) {
+      const int t = threadIdx.x;
+      double s = 0.0;
+#pragma unroll
+      for (int i = 0; i < kW; ++i) s += s_part[i][t];
+      uint64_t* p = lg + ((int64_t)t * E + e) * 2;
+      st_dev(p, tagged((uint32_t)__double2hiint(s), tag));
+      st_dev(p + 1, tagged((uint32_t)__double2loint(s), tag));
+    }
+    __syncthreads();
+  }
+  stamp(a, 1);
+  uint32_t xr[MAXU_GU][F::kXDw];
+  uint4* xl = reinterpret_cast<uint4*>(s_buf);
+  if (B == 1) {
+#pragma unroll
+    for (int j = 0; j < MAXU_GU; ++j)
+      if (lane + kWave * j < UG) F::pack_x(xraw[j], xr[j]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int i = threadIdx.x + q * kW * kWave;
+      if (i < B * UG) {
+        const int t = i / UG, u = i - (i / UG) * UG;
+        uint32_t xs[F::kXDw];
+        F::pack_x(xraw[q], xs);
+#pragma unroll
+        for (int c = 0; c < kCh; ++c)
+          xl[(t * kCh + c) * UG + u] = make_uint4(xs[4 * c], xs[4 * c + 1], xs[4 * c + 2], xs[4 * c + 3]);
+      }
+    }
+  }
+  if (threadIdx.x == 0) {
+    s_jx = (int)(xcd_arrival % (uint32_t)GX);
+    if (a.trace) {
+      a.trace[blockIdx.x * kTracePoints + kTracePoints - 2] = (uint64_t)xcd;
+      a.trace[blockIdx.x * kTracePoints + kTracePoints - 1] = (uint64_t)xcd_arrival;
+    }
+  }
+  stamp(a, 2);
+
+  // Gather every logit (all reads issued before the first wait), then top-k:
+  // wave t handles token t.  Each lane sorts its four candidates; every round
+  // takes the wave-wide best of the lanes' heads and the owner pops it.
+  for (int t = w; t < B; t += kW) {
+    constexpr int kPer = MOE_MAX_EXPERTS / kWave;
+    uint64_t hw[kPer], lw[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int id = lane + kWave * i;
+      if (id < E) {
+        const uint64_t* p = lg + ((int64_t)t * E + id) * 2;
+        hw[i] = ld_dev(p);
+        lw[i] = ld_dev(p + 1);
+      }
+    }
+    {
+      uint64_t wv[2 * kPer];
+      bool valid[2 * kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        wv[2 * i] = hw[i];
+        wv[2 * i + 1] = lw[i];
+        valid[2 * i] = valid[2 * i + 1] = lane + kWave * i < E;
+      }
+      await_tags<2 * kPer>([&](int j) { return lg + ((int64_t)t * E + lane + kWave * (j >> 1)) * 2 + (j & 1); },
+                           wv, valid, tag, wall_clock64(), &s_timeout);
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        hw[i] = wv[2 * i];
+        lw[i] = wv[2 * i + 1];
+      }
+    }
+    if (t == 0) stamp(a, 3);
+    double v[kPer];
+    int id[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      id[i] = lane + kWave * i;
+      v[i] = -__builtin_inf();
+      if (id[i] < E) {
+        v[i] = __hiloint2double((int)payload_of(hw[i]), (int)payload_of(lw[i]));
+      } else {
+        id[i] = 0x7FFFFFFF;
+      }
+    }
+    auto cswap = [&](int p, int q) {
+      if (better(v[q], id[q], v[p], id[p])) {
+        const double tv = v[p];
+        const int ti = id[p];
+        v[p] = v[q];
+        id[p] = id[q];
+        v[q] = tv;
+        id[q] = ti;
+      }
+    };
+    cswap(0, 1);
+    cswap(2, 3);
+    cswap(0, 2);
+    cswap(1, 3);
+    cswap(1, 2);
+    double my_v = 0.0;  // lane r keeps the rank-r selection
+    int my_i = 0;
+    for (int r = 0; r < k; ++r) {
+      double bv = v[0];
+      int bi = id[0];
+      wave_argmax(bv, bi);
+      if (lane == r) {
+        my_v = bv;
+        my_i = bi;
+      }
+      if (id[0] == bi) {  // this lane held the winner: pop it
+        v[0] = v[1];
+        id[0] = id[1];
+        v[1] = v[2];
+        id[1] = id[2];
+        v[2] = v[3];
+        id[2] = id[3];
+        v[3] = -__builtin_inf();
+        id[3] = 0x7FFFFFFF;
+      }
+    }
+    // Softmax over the k selected logits, summed in rank order.
+    const double top = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_v), 0),
+                                        __builtin_amdgcn_readlane(__double2loint(my_v), 0));
+    const double ex = lane < k ? exp(my_v - top) : 0.0;
+    double sum = 0.0;
+    for (int r = 0; r < k; ++r)
+      sum += __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(ex), r),
+                              __builtin_amdgcn_readlane(__double2loint(ex), r));
+    if (lane < k) {
+      my_i = min(max(my_i, 0), E - 1);  // NaN logits can leave no valid candidate: stay in bounds
+      s_idx[t * k + lane] = my_i;
+      s_gw[t * k + lane] = (float)(ex / sum);
+      // bit t: token t picked the expert; bits 8+3t..10+3t: at rank `lane`
+      atomicOr(&s_mask[my_i], (1u << t) | ((uint32_t)lane << (8 + 3 * t)));
+    }
+  }
+  __syncthreads();
+  stamp(a, 4);
+  // Group (token, rank) pairs by expert: experts ascending, tokens ascending.
+  if (w == 0) {
+    int base = 0;
+#pragma unroll
+    for (int q = 0; q < MOE_MAX_EXPERTS / kWave; ++q) {
+      const int ex = q * kWave + lane;
+      const uint32_t mask = ex < E ? s_mask[ex] : 0u;
+      const uint64_t used = __ballot(mask != 0u);
+      if (mask != 0u) {
+        ExpertGroup* gr = &s_grp[base + __popcll(used & ((1ull << lane) - 1ull))];
+        gr->expert = ex;
+        gr->n = __popc(mask & 0xFFu);
+        int p = 0;
+#pragma unroll
+        for (int t = 0; t < kMaxTok; ++t) {
+          if ((mask >> t) & 1u) {
+            gr->tok[p] = t;
+            gr->slot[p] = (int)((mask >> (8 + 3 * t)) & 7u);
+            ++p;
+          }
+        }
+        for (; p < kMaxTok; ++p) {
+          gr->tok[p] = 0;
+          gr->slot[p] = 0;
+        }
+      }
+      base += __popcll(used);
+    }
+    if (lane == 0) s_U = base;
+  }
+  __syncthreads();
+  const int U = s_U;
+  if (g == 0) {
+    for (int i = threadIdx.x; i < S; i += blockDim.x) {
+      if (a.idx_out) a.idx_out[i] = s_idx[i];
+      if (a.gw_out) a.gw_out[i] = s_gw[i];
+    }
+  }
+  stamp(a, 5);
+
+  // ---------------------------------------------------------------- 2. gate / up
+  const int jx = s_jx;     // index inside the XCD
+  const int FS = Fd / NX;  // d_ff slice of this XCD
+  const int f0 = xcd * FS;
+  uint64_t* ht = reinterpret_cast<uint64_t*>(a.ws + a.L.h_tags);  // [S][Fd]
+  {
+    const int RPW = (FS + GX - 1) / GX;  // d_ff rows per workgroup
+    for (int r = w; r < RPW; r += kW) {
+      const int rl = jx * RPW + r;  // row inside the slice
+      if (rl >= FS) break;
+      const int row = f0 + rl;
+      typename F::Raw ring[kRingGU][2][MAXU_GU];
+      auto load_gu = [&](int uu, typename F::Raw(&dst)[2][MAXU_GU]) {
+        const bool live = uu < U;
+        const int ex = s_grp[live ? uu : U - 1].expert;
+        const uint16_t* gs = a.gate.scale ? reinterpret_cast<const uint16_t*>(
+                                                reinterpret_cast<const uint8_t*>(a.gate.scale) + ex * a.gate.scale_stride)
+                                          : nullptr;
+        const uint16_t* us = a.up.scale ? reinterpret_cast<const uint16_t*>(
+                                              reinterpret_cast<const uint8_t*>(a.up.scale) + ex * a.up.scale_stride)
+                                        : nullptr;
+        const typename F::Row rg = F::row(a.gate.base + ex * a.gate.stride, gs, row, D);
+        const typename F::Row ru = F::row(a.up.base + ex * a.up.stride, us, row, D);
+#pragma unroll
+        for (int j = 0; j < MAXU_GU; ++j) {
+          const int u = lane + kWave * j;
+          const int ul = (live && u < UG) ? u : 0;
+          F::load(rg, ul, dst[0][j]);
+          F::load(ru, ul, dst[1][j]);
+        }
+      };
+      auto compute_gu = [&](int uu, const typename F::Raw(&src)[2][MAXU_GU]) {
+        consume(src);
+        const int n = s_grp[uu].n;
+        for (int i = 0; i < n; ++i) {
+          const int t = s_grp[uu].tok[i];
+          float ag = 0.0f, au = 0.0f;
+#pragma unroll
+          for (int j = 0; j < MAXU_GU; ++j) {
+            const int u = lane + kWave * j;
+            if (u < UG) {
+              if (B == 1) {
+                ag += F::gu_dot(src[0][j], (uint32_t)u & 3u, xr[j]);
+                au += F::gu_dot(src[1][j], (uint32_t)u & 3u, xr[j]);
+              } else {
+                uint32_t xs[F::kXDw];
+#pragma unroll
+                for (int c = 0; c < kCh; ++c) {
+                  const uint4 p = xl[(t * kCh + c) * UG + u];
+                  xs[4 * c] = p.x;
+                  xs[4 * c + 1] = p.y;
+                  xs[4 * c + 2] = p.z;
+                  xs[4 * c + 3] = p.w;
+                }
+                ag += F::gu_dot(src[0][j], (uint32_t)u & 3u, xs);
+                au += F::gu_dot(src[1][j], (uint32_t)u & 3u, xs);
+              }
+            }
+          }
+          ag = wave_sum_dpp(ag);
+          au = wave_sum_dpp(au);
+          if (lane == 63) s_hv[w][t * k + s_grp[uu].slot[i]] = silu(ag) * au;
+        }
+      };
+#pragma unroll
+      for (int j = 0; j < kRingGU - 1; ++j) {
+        load_gu(j, ring[j]);
+        __builtin_amdgcn_sched_barrier(0);  // slots are requested in ring order
+      }
+      for (int base = 0; base < U; base += kRingGU) {
+#pragma unroll
+        for (int j = 0; j < kRingGU; ++j) {
+          load_gu(base + j + kRingGU - 1, ring[(j + kRingGU - 1) % kRingGU]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (base + j < U)
+            compute_gu(base + j, ring[j]);
+          else
+            consume(ring[j]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // Publish this row of h for every slot (each slot belongs to one group).
+      for (int s = lane; s < S; s += kWave) st_dev(ht + (int64_t)s * Fd + row, tagged(__float_as_uint(s_hv[w][s]), tag));
+    }
+  }
+  stamp(a, 6);
+
+  // ---------------------------------------------------------------- 3. down (partials over the slice)
+  // LDS views: h slice per slot, unit blocks padded by 4 floats (conflict-free
+  // float4 reads; Q2_K keeps its sub-block sums there), then the per-slot row
+  // partials.
+  constexpr int kHB = F::kUnitW + 4;
+  float* sh = reinterpret_cast<float*>(s_buf);  // [S][UPS][kHB]
+  float* syp = sh + (size_t)S * UPS * kHB;       // [S][rows of this workgroup]
+  const int RPWd = (D + GX - 1) / GX;            // output rows per workgroup
+  const int RPV = (RPWd + kW - 1) / kW;          // rows per wave
+  const int n0 = jx * RPWd;
+  const int UD = RPV * UPS;                      // (row, slice-unit) pairs per wave per expert
+  const int ub = lane % UPS;                     // this lane's unit inside the slice row
+  // Where this lane's down unit lives: unit xcd*UPS + ub of row n, or, in
+  // the tiled layout, unit (xcd*UPS + ub) % UPT of row c*D + n of the
+  // [(Fd/256)*D][256] matrix, c = (xcd*UPS + ub) / UPT.
+  constexpr int UPT = kTileCols / F::kUnitW;
+  const int du_row = xcd * UPS + ub;
+  const int dunit = a.down.tiled ? du_row % UPT : du_row;
+  const int64_t drow0 = a.down.tiled ? (int64_t)(du_row / UPT) * D : 0;
+  const int dK = a.down.tiled ? kTileCols : Fd;
+  const uint32_t dsh = (uint32_t)dunit & 3u;
+  typename F::Raw dring[kRingDN][MAXU_DN];
+  auto load_dn = [&](int uu, typename F::Raw(&dst)[MAXU_DN]) {
+    const bool live = uu < U;
+    const int ex = s_grp[live ? uu : U - 1].expert;
+    const uint16_t* ds = a.down.scale ? reinterpret_cast<const uint16_t*>(
+                                            reinterpret_cast<const uint8_t*>(a.down.scale) + ex * a.down.scale_stride)
+                                      : nullptr;
+#pragma unroll
+    for (int j = 0; j < MAXU_DN; ++j) {
+      const int v = lane + kWave * j;
+      const int rloc = w * RPV + v / UPS;
+      const bool ok = live && v < UD && rloc < RPWd && n0 + rloc < D;
+      const typename F::Row rw = F::row(a.down.base + ex * a.down.stride, ds, ok ? drow0 + n0 + rloc : 0, dK);
+      F::load(rw, ok ? dunit : 0, dst[j]);
+    }
+  };
+  auto compute_dn = [&](int uu, const typename F::Raw(&src)[MAXU_DN]) {
+    consume(src);
+    const int n = s_grp[uu].n;
+    for (int i = 0; i < n; ++i) {
+      const int s = s_grp[uu].tok[i] * k + s_grp[uu].slot[i];
+      const float* hx = sh + (s * UPS + ub) * kHB;
+#pragma unroll
+      for (int j = 0; j < MAXU_DN; ++j) {
+        const int v = lane + kWave * j;
+        const int rloc = w * RPV + v / UPS;
+        const bool ok = v < UD && rloc < RPWd && n0 + rloc < D;
+        float pr = ok ? F::dn_dot(src[j], dsh, hx) : 0.0f;
+        pr = group_sum_dpp<UPS>(pr);
+        if (ok && ub == 0) syp[s * RPWd + rloc] = pr;
+      }
+    }
+  };
+  __syncthreads();  // the activation view of s_buf is no longer used
+  // The first experts' down weights are requested before waiting for h.
+#pragma unroll
+  for (int j = 0; j < kRingDN - 1; ++j) {
+    load_dn(j, dring[j]);
+    __builtin_amdgcn_sched_barrier(0);  // slots are requested in ring order
+  }
+  {
+    // Gather this XCD's h slice for every slot (written by the XCD's workgroups).
+    const uint64_t t0 = wall_clock64();
+    const int total = S * FS;
+    for (int i0 = threadIdx.x; i0 < total; i0 += kSpinBatch * kW * kWave) {
+      auto hptr = [&](int q) {
+        const int i = i0 + q * kW * kWave;
+        return ht + (int64_t)(i / FS) * Fd + f0 + (i - (i / FS) * FS);
+      };
+      uint64_t v[kSpinBatch];
+      bool valid[kSpinBatch];
+#pragma unroll
+      for (int q = 0; q < kSpinBatch; ++q) {
+        valid[q] = i0 + q * kW * kWave < total;
+        v[q] = valid[q] ? ld_xcd(hptr(q)) : 0ull;
+      }
+      await_tags<kSpinBatch>(hptr, v, valid, tag, t0, &s_timeout);
+#pragma unroll
+      for (int q = 0; q < kSpinBatch; ++q) {
+        const int i = i0 + q * kW * kWave;
+        if (valid[q]) {
+          const int s = i / FS, f = i - (i / FS) * FS;
+          sh[(s * UPS + f / F::kUnitW) * kHB + f % F::kUnitW] = __uint_as_float(payload_of(v[q]));
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < S * UPS; i += kW * kWave) F::prep_h(sh + i * kHB);
+    __syncthreads();
+  }
+  stamp(a, 7);
+  for (int base = 0; base < U; base += kRingDN) {
+#pragma unroll
+    for (int j = 0; j < kRingDN; ++j) {
+      load_dn(base + j + kRingDN - 1, dring[(j + kRingDN - 1) % kRingDN]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (base + j < U)
+        compute_dn(base + j, dring[j]);
+      else
+        consume(dring[j]);
+    }
+  }
+  __syncthreads();
+  stamp(a, 8);
+  // Combine the k ranks in rank order and publish this XCD's partial rows.
+  {
+    uint64_t* pt = reinterpret_cast<uint64_t*>(a.ws + a.L.part_tags);  // [NX][B][D]
+    for (int i = threadIdx.x; i < B * RPWd; i += blockDim.x) {
+      const int t = i / RPWd, rl = i - (i / RPWd) * RPWd;
+      const int n = n0 + rl;
+      if (n < D) {
+        float acc = 0.0f;
+        for (int j = 0; j < k; ++j) acc = __builtin_fmaf(s_gw[t * k + j], syp[(t * k + j) * RPWd + rl], acc);
+        st_dev(pt + ((int64_t)xcd * B + t) * D + n, tagged(__float_as_uint(acc), tag));
+      }
+    }
+  }
+  stamp(a, 9);
+
+  // ---------------------------------------------------------------- finish: sum the NX partials
+  {
+    const uint64_t* pt = reinterpret_cast<const uint64_t*>(a.ws + a.L.part_tags);
+    const int RF = (RPWd + NX - 1) / NX;  // rows this workgroup finishes
+    const int rf0 = xcd * RF;
+    const uint64_t t0 = wall_clock64();
+    for (int i = threadIdx.x; i < B * RF; i += blockDim.x) {
+      const int t = i / RF, rl = rf0 + (i - (i / RF) * RF);
+      const int n = n0 + rl;
+      if (rl < RPWd && n < D) {
+        auto pptr = [&](int x) { return pt + ((int64_t)x * B + t) * D + n; };
+        uint64_t v[kMaxNX];
+        bool valid[kMaxNX];
+#pragma unroll
+        for (int x = 0; x < kMaxNX; ++x) {
+          valid[x] = x < NX;
+          v[x] = valid[x] ? ld_dev(pptr(x)) : 0ull;
+        }
+        await_tags<kMaxNX>(pptr, v, valid, tag, t0, &s_timeout);
+        float acc = 0.0f;
+#pragma unroll
+        for (int x = 0; x < kMaxNX; ++x)
+          if (x < NX) acc += __uint_as_float(payload_of(v[x]));
+        if (a.residual) acc += a.residual[(int64_t)t * D + n];
+        a.y[(int64_t)t * D + n] = acc;
+      }
+    }
+  }
+  __syncthreads();
+  stamp(a, 10);
+  if (threadIdx.x == 0) {
+    if (s_timeout) __hip_atomic_fetch_or(ctr + kCtrTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Every workgroup has read the epoch before workgroup 0 gets here
+    // (workgroup 0 consumed the logits of all of them), so advance it.
+    if (g == 0) ctr[kCtrEpoch] = tag;
+  }
+}
+
+template <class F, int MAXU_GU, int MAXU_DN, int UPS>
+hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS>), dim3(grid), dim3(kW * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+template <class F, int UPS>
+hipError_t launch_fused_f(const FusedArgs& a, int grid, int gu_units, int dn_units, hipStream_t s) {
+  if (gu_units > kWave) {
+    return dn_units > kWave ? launch_fused_t<F, 2, 2, UPS>(a, grid, s) : launch_fused_t<F, 2, 1, UPS>(a, grid, s);
+  }
+  return dn_units > kWave ? launch_fused_t<F, 1, 2, UPS>(a, grid, s) : launch_fused_t<F, 1, 1, UPS>(a, grid, s);
+}
+
+template <class F>
+hipError_t launch_fused_ups(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s) {
+  switch (ups) {
+    case 1: return launch_fused_f<F, 1>(a, grid, gu_units, dn_units, s);
+    case 2: return launch_fused_f<F, 2>(a, grid, gu_units, dn_units, s);
+    case 4: return launch_fused_f<F, 4>(a, grid, gu_units, dn_units, s);
+    case 8: return launch_fused_f<F, 8>(a, grid, gu_units, dn_units, s);
+    case 16: return launch_fused_f<F, 16>(a, grid, gu_units, dn_units, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// One instantiation set per weight format (each in its own translation unit).
+hipError_t launch_mx(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
+hipError_t launch_q2k(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
+hipError_t launch_int4(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
+
+}  // namespace fused
+}  // namespace moe

@@ -26,7 +26,29 @@ __device__ __forceinline__ void rows_dot(const typename F::Row (&rows)[R], int K
 #pragma unroll
     for (int r = 0; r < R; ++r) F::load(rows[r], u, raw[r]);
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] += F::dot(raw[r], x + (int64_t)F::kUnitW * u);
+    for (int r = 0; r < R; ++r) acc[r] += F::dot(raw[r], (uint32_t)u & 3u, x + (int64_t)F::kUnitW * u);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+}
+
+// Same for rows n[r] of a matrix [N][K] stored in MOE_LAYOUT_TILE256: unit u
+// of row n is unit u % UPT of row (u / UPT) * N + n of the [(K/256)*N][256]
+// matrix.
+template <class F, int R>
+__device__ __forceinline__ void rows_dot_tiled(const uint8_t* base, const uint16_t* sc, const int (&n)[R], int N,
+                                               int K, const float* __restrict__ x, float (&acc)[R]) {
+  constexpr int UPT = kTileCols / F::kUnitW;
+  const int U = F::units(K);
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int u = lane_id(); u < U; u += kWave) {
+    const int c = u / UPT, uu = u % UPT;
+    typename F::Raw raw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) F::load(F::row(base, sc, (int64_t)c * N + n[r], kTileCols), uu, raw[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] += F::dot(raw[r], (uint32_t)uu & 3u, x + (int64_t)F::kUnitW * u);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
@@ -119,14 +141,21 @@ __global__ __launch_bounds__(256) void down_kernel(WeightRef down, int D, int Fd
                                         reinterpret_cast<const uint8_t*>(down.scale) + grp.expert * down.scale_stride)
                                   : nullptr;
   typename F::Row rows[kDownR];
+  int rn[kDownR];
 #pragma unroll
-  for (int r = 0; r < kDownR; ++r) rows[r] = F::row(dbase, ds, min(row0 + r, D - 1), Fd);
+  for (int r = 0; r < kDownR; ++r) {
+    rn[r] = min(row0 + r, D - 1);
+    rows[r] = F::row(dbase, ds, rn[r], Fd);
+  }
   const float* h = reinterpret_cast<const float*>(ws + L.h);
   float* yp = reinterpret_cast<float*>(ws + L.yp);
   for (int t = 0; t < grp.n; ++t) {
     const int64_t ts = (int64_t)grp.tok[t] * k + grp.slot[t];
     float acc[kDownR];
-    rows_dot<F, kDownR>(rows, Fd, h + ts * Fd, acc);
+    if (down.tiled)
+      rows_dot_tiled<F, kDownR>(dbase, ds, rn, D, Fd, h + ts * Fd, acc);
+    else
+      rows_dot<F, kDownR>(rows, Fd, h + ts * Fd, acc);
     if (lane_id() == 0) {
 #pragma unroll
       for (int r = 0; r < kDownR; ++r)

@@ -184,7 +184,11 @@ struct WeightRef {
   const uint16_t* scale;    // INT4 scales (else null)
   int64_t stride;           // bytes between experts
   int64_t scale_stride;     // bytes between experts' scales
+  int tiled;                // 1: MOE_LAYOUT_TILE256 (row c*N + n of a [(K/256)*N][256] matrix), 0: row-major
 };
+
+// Columns per tile of MOE_LAYOUT_TILE256.
+constexpr int kTileCols = 256;
 
 hipError_t launch_gemv(int fmt, const void* w0, const uint16_t* scale, int N, int K, const float* x,
                        int B, float* y, hipStream_t s);
@@ -210,6 +214,11 @@ hipError_t launch_quantize_int4(const uint8_t* mx, int64_t ngroups, int32_t* q, 
 hipError_t launch_validate_mxfp4(const uint8_t* blocks, int64_t n, int32_t* bad, hipStream_t s);
 
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
+
+// dst[(c*N + n)*tile + i] = src[n*tiles*tile + c*tile + i] for c < tiles,
+// n < N, i < tile (elements of 2 or 4 bytes).
+hipError_t launch_tile_rows(const void* src, void* dst, int64_t N, int tiles, int tile_elems, int elem_bytes,
+                            hipStream_t s);
 
 // Single-launch layer (routing, gate/up, down and combine in one kernel).
 struct FusedShape {

@@ -62,9 +62,11 @@ class Layer:
     side converts its own twin bytes with oracle.quantize_fp4_to_int4g32.
     """
 
-    def __init__(self, fmt: str, seed: int, layer: int, E: int, D: int, F: int, top_k: int = 6):
+    def __init__(self, fmt: str, seed: int, layer: int, E: int, D: int, F: int, top_k: int = 6,
+                 down_layout: str = "rows"):
         self.fmt, self.seed, self.layer = fmt, seed, layer
         self.E, self.D, self.F, self.k = E, D, F, top_k
+        self.down_layout = down_layout
         self.router = synth.router_weights(seed, layer, E, D)
         self.router_dev = dev(self.router)
         src = "mxfp4" if fmt == "int4g32" else fmt
@@ -93,15 +95,29 @@ class Layer:
                                                 s.data_ptr() + e * sstride)
                 self.q[proj] = (q, qstride, s, sstride)
             del self.bytes
+            if down_layout == "tile256":  # same buffers' shapes, blocks permuted per expert
+                q, qstride, sc, sstride = self.q[synth.PROJ_DOWN]
+                qt, st = torch.empty_like(q), torch.empty_like(sc)
+                for e in range(E):
+                    moe.moe_tile_weights("int4g32", q.data_ptr() + e * qstride, D, F, qt.data_ptr() + e * qstride,
+                                         src_scale=sc.data_ptr() + e * sstride, dst_scale=st.data_ptr() + e * sstride)
+                self.q[synth.PROJ_DOWN] = (qt, qstride, st, sstride)
             torch.cuda.synchronize()
             self.desc = moe.make_layer_desc(
                 fmt, self.router_dev, self.q[0][0], self.q[1][0], self.q[2][0], E, D, F, top_k,
                 self.q[0][1], self.q[1][1], self.q[2][1], self.q[0][2], self.q[1][2], self.q[2][2],
-                self.q[0][3], self.q[1][3], self.q[2][3])
+                self.q[0][3], self.q[1][3], self.q[2][3], down_layout=down_layout)
         else:
+            if down_layout == "tile256":
+                buf, stride = self.bytes[synth.PROJ_DOWN]
+                bt = torch.empty_like(buf)
+                for e in range(E):
+                    moe.moe_tile_weights(fmt, buf.data_ptr() + e * stride, D, F, bt.data_ptr() + e * stride)
+                self.bytes[synth.PROJ_DOWN] = (bt, stride)
+                torch.cuda.synchronize()
             self.desc = moe.make_layer_desc(
                 fmt, self.router_dev, self.bytes[0][0], self.bytes[1][0], self.bytes[2][0], E, D, F, top_k,
-                self.bytes[0][1], self.bytes[1][1], self.bytes[2][1])
+                self.bytes[0][1], self.bytes[1][1], self.bytes[2][1], down_layout=down_layout)
         self._cache = {}
 
     # -- oracle side: regenerate expert e's bytes with the host twin

@@ -36,13 +36,18 @@ def test_header_declares_the_boundary():
     assert set(names) == set(moe.EXPORTS), set(names) ^ set(moe.EXPORTS)
 
 
+def test_trace_record_size_matches_header():
+    m = re.search(r"#define MOE_TRACE_FIELDS (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == moe.TRACE_FIELDS
+
+
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L, name), name
 
 
 def test_abi_version_and_status_strings(L):
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     for st in range(7):
         assert moe.moe_status_string(st)
     assert moe.moe_status_string(0) == "ok"
@@ -97,6 +102,25 @@ def test_layer_and_route_validation_on_host(L):
     assert L.quantize_fp4_to_int4g32(FAKE, 8, 48, FAKE, FAKE, None) == 2
     assert L.quantize_fp4_to_int4g32(FAKE, 8, 64, FAKE + 4, FAKE, None) == 6
     assert L.moe_validate_mxfp4(FAKE, -1, FAKE, None) == 1
+
+
+def test_layout_validation_on_host(L):
+    d = moe.make_layer_desc("mxfp4", FAKE, FAKE, FAKE, FAKE, 256, 4096, 2048, 6, 4456704, 4456704, 4456704,
+                            down_layout="tile256")
+    ws_ok = 1 << 30
+    d.down_layout = 7                                   # not a layout
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, ws_ok, None, None, None) == 1
+    d.down_layout, d.d_ff = 1, 2080                     # tiles need d_ff % 256 == 0
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, ws_ok, None, None, None) == 2
+    T = L.moe_tile_weights
+    assert T(3, FAKE, None, 8, 256, FAKE, None, None) == 1           # bad format
+    assert T(0, None, None, 8, 256, FAKE, None, None) == 1           # null source
+    assert T(0, FAKE, None, 0, 256, FAKE, None, None) == 1           # N < 1
+    assert T(0, FAKE, None, 8, 224, FAKE, None, None) == 2           # K % 256
+    assert T(1, FAKE, None, 8, 512, FAKE + 2, None, None) == 6       # misaligned destination
+    assert T(2, FAKE, None, 8, 256, FAKE, None, None) == 1           # INT4 without scales
+    assert T(0, FAKE, FAKE, 8, 256, FAKE, FAKE, None) == 1           # scales only for INT4
+    assert T(2, FAKE + 4, FAKE, 8, 256, FAKE, FAKE, None) == 6       # INT4 codes 16-byte aligned
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -2,6 +2,9 @@
 the fp64 oracle, in all three formats, at small shapes and at the full layer
 shape (256 experts, d_model 4096, d_ff 2048, top-6) for B = 1 and B = 8.
 
+Both down-projection layouts (row-major as published, and 256-column tiles)
+are covered; the full-shape Q2_K and INT4 runs use the tiled layout.
+
 Invariants: run-to-run bitwise determinism, identical tokens give identical
 rows (and 6 unique experts), and a token's result does not depend on the
 batch width (B=8 row t == B=1 run of token t, bitwise)."""
@@ -17,13 +20,13 @@ pytestmark = pytest.mark.gpu
 _LAYERS = {}
 
 
-def layer(fmt, E, D, F, k=6, seed=0x5EED, lid=0):
-    key = (fmt, E, D, F, k, seed, lid)
+def layer(fmt, E, D, F, k=6, seed=0x5EED, lid=0, down_layout="rows"):
+    key = (fmt, E, D, F, k, seed, lid, down_layout)
     if key not in _LAYERS:
-        if len(_LAYERS) > 3:  # keep device memory bounded across the module
+        if len(_LAYERS) > 2:  # keep device memory bounded across the module
             _LAYERS.clear()
             torch.cuda.empty_cache()
-        _LAYERS[key] = Layer(fmt, seed, lid, E, D, F, k)
+        _LAYERS[key] = Layer(fmt, seed, lid, E, D, F, k, down_layout=down_layout)
     return _LAYERS[key]
 
 
@@ -35,20 +38,32 @@ def _parity(L, xb, what):
     return assert_parity(y, yo, what=what), y
 
 
+@pytest.mark.parametrize("layout", ["rows", "tile256"])
 @pytest.mark.parametrize("fmt", ["mxfp4", "q2k", "int4g32"])
 @pytest.mark.parametrize("B", [1, 3, 8])
-def test_layer_small(fmt, B):
-    L = layer(fmt, 32, 512, 256, 6, seed=11)
+def test_layer_small(fmt, B, layout):
+    L = layer(fmt, 32, 512, 256, 6, seed=11, down_layout=layout)
     xb = synth.token_bf16(500 + B, B, 512)
-    _parity(L, xb, f"{fmt} small B={B}")
+    _parity(L, xb, f"{fmt} small B={B} {layout}")
 
 
-def test_layer_multi_launch_fallback_shape():
+@pytest.mark.parametrize("layout", ["rows", "tile256"])
+def test_layer_small_several_tiles(layout):
+    # d_ff 1024: four 256-column tiles per down row (two per XCD slice on an
+    # 8-XCD chip would need d_ff 4096; here slices are smaller than a tile)
+    L = layer("mxfp4", 24, 256, 1024, 4, seed=21, down_layout=layout)
+    for B in (1, 5):
+        _parity(L, synth.token_bf16(550 + B, B, 256), f"d_ff 1024 B={B} {layout}")
+
+
+@pytest.mark.parametrize("layout", ["rows", "tile256"])
+def test_layer_multi_launch_fallback_shape(layout):
     # d_model 8192 has more MXFP4 blocks per row than the single-launch
     # kernel keeps per lane, so the layer runs as separate launches.
-    L = layer("mxfp4", 16, 8192, 256, 6, seed=13)
+    L = layer("mxfp4", 16, 8192, 512, 6, seed=13, down_layout=layout)
+    assert not _single_launch(L, 1)
     for B in (1, 8):
-        _parity(L, synth.token_bf16(700 + B, B, 8192), f"fallback B={B}")
+        _parity(L, synth.token_bf16(700 + B, B, 8192), f"fallback B={B} {layout}")
 
 
 def test_layer_small_ragged_topk_and_experts():
@@ -57,19 +72,20 @@ def test_layer_small_ragged_topk_and_experts():
         _parity(L, synth.token_bf16(600 + B, B, 96), f"ragged B={B}")
 
 
+@pytest.mark.parametrize("layout", ["rows", "tile256"])
 @pytest.mark.parametrize("B", [1, 8])
-def test_layer_full_mxfp4(B):
-    L = layer("mxfp4", 256, 4096, 2048)
-    err, y = _parity(L, synth.token_bf16(1000 + B, B, 4096), f"mxfp4 full B={B}")
-    print(f"mxfp4 layer B={B}: max rel-inf err {err:.3e}")
+def test_layer_full_mxfp4(B, layout):
+    L = layer("mxfp4", 256, 4096, 2048, down_layout=layout)
+    err, y = _parity(L, synth.token_bf16(1000 + B, B, 4096), f"mxfp4 full B={B} {layout}")
+    print(f"mxfp4 layer B={B} {layout}: max rel-inf err {err:.3e}")
 
 
 @pytest.mark.parametrize("fmt", ["q2k", "int4g32"])
 @pytest.mark.parametrize("B", [1, 8])
 def test_layer_full_other_formats(fmt, B):
-    L = layer(fmt, 256, 4096, 2048)
-    err, y = _parity(L, synth.token_bf16(2000 + B, B, 4096), f"{fmt} full B={B}")
-    print(f"{fmt} layer B={B}: max rel-inf err {err:.3e}")
+    L = layer(fmt, 256, 4096, 2048, down_layout="tile256")
+    err, y = _parity(L, synth.token_bf16(2000 + B, B, 4096), f"{fmt} full B={B} tile256")
+    print(f"{fmt} layer B={B} tile256: max rel-inf err {err:.3e}")
 
 
 def _single_launch(L, B):
@@ -79,8 +95,9 @@ def _single_launch(L, B):
     return moe.moe_layer_decode_traced(L.desc, x, y, L.workspace(B)) is not None
 
 
-def test_layer_invariants_full_shape():
-    L = layer("mxfp4", 256, 4096, 2048)
+@pytest.mark.parametrize("layout", ["rows", "tile256"])
+def test_layer_invariants_full_shape(layout):
+    L = layer("mxfp4", 256, 4096, 2048, down_layout=layout)
     assert _single_launch(L, 1) and _single_launch(L, 8), "full layer shape should run as one launch"
     x8 = synth.token_bf16(3000, 8, 4096)
     ws = L.workspace(8)
@@ -96,3 +113,33 @@ def test_layer_invariants_full_shape():
     assert all(np.array_equal(ys[0], ys[t]) for t in range(8))
     assert len(np.unique(is_)) == 6
     assert np.array_equal(ys[0], y8a[0])
+
+
+def test_traced_records_stay_in_bounds():
+    """The traced entry point writes exactly MOE_TRACE_FIELDS words per
+    workgroup: rows past the last workgroup keep their sentinel, time stamps
+    of a workgroup do not decrease, and the XCD field is a small index."""
+    import ctypes
+
+    import quantized_moe_decode_route_amd as moe
+    L = layer("mxfp4", 32, 512, 256, 6, seed=11)
+    x = torch.from_numpy(synth.token_bf16(77, 2, 512).view(np.int16)).to("cuda")
+    y = torch.empty((2, 512), dtype=torch.float32, device="cuda")
+    ws = L.workspace(2)
+    nb = ctypes.c_int(0)
+    lib = moe.lib()
+    args = (ctypes.byref(L.desc), x.data_ptr(), 2, y.data_ptr(), ws.data_ptr(), ws.numel())
+    assert lib.moe_layer_decode_traced(*args, None, ctypes.byref(nb), None) == 0
+    assert nb.value > 0
+    guard = 4
+    tr = torch.full((nb.value + guard, moe.TRACE_FIELDS), -1, dtype=torch.int64, device="cuda")
+    tr[:nb.value].zero_()
+    stream = torch.cuda.current_stream().cuda_stream
+    assert lib.moe_layer_decode_traced(*args, tr.data_ptr(), ctypes.byref(nb), stream) == 0
+    torch.cuda.synchronize()
+    t = tr.cpu().numpy()
+    assert (t[nb.value:] == -1).all(), "trace writes past the last workgroup's record"
+    stamps = t[:nb.value, :11]
+    assert (stamps > 0).all() and (np.diff(stamps, axis=1) >= 0).all()
+    assert (t[:nb.value, 11:14] == 0).all()
+    assert (t[:nb.value, 14] < 16).all()
