@@ -176,9 +176,11 @@ int moe_layer_decode_profiled(const moe_layer_desc* L, const uint16_t* x_bf16, i
  * the caller) receives, per workgroup, in slots 0..10 the 100 MHz wall clock
  * at: start, own router logits published, activations staged, all logits
  * gathered (wave 0), top-k done, grouping done, gate/up done, h slice
- * gathered, down done, partial outputs published, end; slots 11..13 are
- * reserved; slot 14 is the workgroup's XCD and slot 15 the raw value of its
- * XCD arrival counter. */
+ * gathered, down done, partial outputs published, end; slot 11 the clock
+ * when the h gather starts and slot 12 when its reads are complete; slot 13
+ * the re-read passes thread 0 needed in the logit wait (bits 0..15) and in
+ * the h waits (bits 16..31); slot 14 is the workgroup's XCD and slot 15 the
+ * raw value of its XCD arrival counter. */
 #define MOE_TRACE_FIELDS 16 /* uint64 per workgroup in moe_layer_decode_traced */
 int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
                             size_t ws_bytes, uint64_t* trace, int* trace_blocks, void* stream);

@@ -38,9 +38,9 @@ FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx) {
   sh.dn_units = rpv * ups;
   if (sh.dn_units > 2 * kWave) return sh;
   sh.ups = ups;
-  // LDS: activations (B > 1) during gate/up, then h slices and row partials.
+  // LDS: activations during gate/up, then h slices and row partials.
   const size_t staged = fmt == MOE_FMT_Q2K ? 4 * Q2kFmt::kXDw : fmt == MOE_FMT_INT4G32 ? 4 * Int4Fmt::kXDw : 4 * MxFmt::kXDw;
-  const size_t act = B > 1 ? (size_t)B * (D / uw) * staged : 0;
+  const size_t act = (size_t)B * (D / uw) * staged;
   const size_t down = (size_t)B * k * ups * (uw + 4) * 4 + (size_t)B * k * rpwd * 4;
   if (act > (size_t)kLdsBytes || down > (size_t)kLdsBytes) return sh;
   sh.ok = true;

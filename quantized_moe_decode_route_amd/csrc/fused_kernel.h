@@ -149,7 +149,39 @@ __device__ __forceinline__ void wave_argmax(double& v, int& i) {
   v = __hiloint2double(hi, lo);
 }
 
+// Top 32 bits of the order-preserving integer image of a double: a > b
+// implies order_key32(a) >= order_key32(b).
+__device__ __forceinline__ uint32_t order_key32(double v) {
+  const uint32_t hi = (uint32_t)__double2hiint(v);
+  return (hi & 0x80000000u) ? ~hi : (hi | 0x80000000u);
+}
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  // lanes without a source read 0, the identity of the unsigned maximum
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Wave-wide unsigned maximum, returned uniformly.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));
+  v = max(v, dpp_u<0x4E>(v));
+  v = max(v, dpp_u<0x141>(v));
+  v = max(v, dpp_u<0x140>(v));
+  v = max(v, dpp_u<0x142, 0xA>(v));
+  v = max(v, dpp_u<0x143, 0xC>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// One selected expert of a layer call: bit t of `mask` (t < 8) is set when
+// token t picked the expert, bits 8+3t .. 10+3t hold its rank in that token's
+// top-k.
+struct LayerGroup {
+  int32_t expert;
+  uint32_t mask;
+};
 
 struct FusedArgs {
   const float* router_w;
@@ -190,18 +222,19 @@ __device__ __forceinline__ void consume(const T& raw) {
 // re-reads all stale words together, so one pass costs one memory round trip
 // however many words were stale.
 template <int N, class Addr>
-__device__ __forceinline__ void await_tags(Addr addr, uint64_t (&v)[N], const bool (&valid)[N], uint32_t tag,
-                                           uint64_t t0, int* timeout) {
+__device__ __forceinline__ int await_tags(Addr addr, uint64_t (&v)[N], const bool (&valid)[N], uint32_t tag,
+                                          uint64_t t0, int* timeout) {
   static_assert(N <= 32, "stale words are tracked in a 32-bit mask");
+  int rereads = 0;  // passes that had to read again (reported by the traced entry point)
 #pragma nounroll
-  for (;;) {
+  for (;; ++rereads) {
     uint32_t stale = 0u;
 #pragma unroll
     for (int i = 0; i < N; ++i) stale |= (valid[i] && tag_of(v[i]) != tag) ? (1u << i) : 0u;
-    if (stale == 0u) return;
+    if (stale == 0u) return rereads;
     if (wall_clock64() - t0 > kSpinTicks) {
       *timeout = 1;
-      return;
+      return rereads;
     }
     __builtin_amdgcn_s_sleep(1);
     uint64_t again[N];  // every word is re-read (all requests first); stale ones take the new value
@@ -221,13 +254,23 @@ constexpr int kLdsBytes = 128 * 1024;
 // wave wait for every load in flight), and every load is issued
 // unconditionally (past the last expert, one cached unit for the whole wave)
 // so the number of loads between a load and its use is fixed.
-constexpr int kRingGU = 4;
-constexpr int kRingDN = 6;
+template <class F>
+struct Rings {  // per format, so a format with more live registers can use shallower rings
+  static constexpr int kGU = 4;
+  static constexpr int kDN = 7;  // six experts (all of them at B=1) requested ahead
+};
+template <>
+struct Rings<Int4Fmt> {  // its gate/up unpacking keeps more registers live
+  static constexpr int kGU = 4;
+  static constexpr int kDN = 6;
+};
 constexpr int kSpinBatch = 12;  // tagged words a thread reads before its first wait
 
 template <class F, int MAXU_GU, int MAXU_DN, int UPS>
 __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a) {
   constexpr int kCh = F::kXDw / 4;  // 16-byte chunks of one unit's staged activations
+  constexpr int kRingGU = Rings<F>::kGU;
+  constexpr int kRingDN = Rings<F>::kDN;
   const int G = gridDim.x;
   const int g = blockIdx.x;
   const int w = threadIdx.x / kWave;
@@ -241,7 +284,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 
   __shared__ int32_t s_idx[kMaxSlots];
   __shared__ float s_gw[kMaxSlots];
-  __shared__ ExpertGroup s_grp[kMaxSlots];
+  __shared__ LayerGroup s_grp[kMaxSlots];
   __shared__ uint32_t s_mask[MOE_MAX_EXPERTS];  // per expert: tokens that picked it and at which rank
   __shared__ double s_part[kW][kMaxTok];
   __shared__ float s_hv[kW][kMaxSlots];  // a wave's h values for its current row, per slot
@@ -257,6 +300,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // The result is first used after the router logits, so its latency hides
   // behind them.
   uint32_t xcd_arrival = 0;
+  int trace_rereads = 0;  // thread 0: re-read passes of the logit (low half) and h (high half) waits
   if (threadIdx.x == 0) {
     s_timeout = 0;
     xcd_arrival = __hip_atomic_fetch_add(ctr + kCtrXcdBase + xcd, 1u, __ATOMIC_RELAXED,
@@ -264,24 +308,15 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
   for (int i = threadIdx.x; i < MOE_MAX_EXPERTS; i += blockDim.x) s_mask[i] = 0u;
 
-  // Activations for gate/up: requested now, staged after the router logits
-  // (registers for one token; LDS [t][chunk][unit] for several, so lanes read
-  // consecutive chunks).  B * units <= 2 * blockDim for every shape this
-  // kernel accepts.
+  // Activations for gate/up: requested now, staged in LDS ([t][chunk][unit],
+  // so lanes read consecutive chunks) after the router logits.  B * units <=
+  // 2 * blockDim for every shape this kernel accepts.
   const int UG = F::units(D);
   uint32_t xraw[2][F::kXRaw];
-  if (B == 1) {
 #pragma unroll
-    for (int j = 0; j < MAXU_GU && j < 2; ++j) {
-      const int u = lane + kWave * j;
-      if (u < UG) F::load_x(a.x, u, xraw[j]);
-    }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = threadIdx.x + q * kW * kWave;
-      if (i < B * UG) F::load_x(a.x + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);
-    }
+  for (int q = 0; q < 2; ++q) {
+    const int i = threadIdx.x + q * kW * kWave;
+    if (i < B * UG) F::load_x(a.x + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);
   }
   __syncthreads();
 
@@ -333,24 +368,17 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     __syncthreads();
   }
   stamp(a, 1);
-  uint32_t xr[MAXU_GU][F::kXDw];
   uint4* xl = reinterpret_cast<uint4*>(s_buf);
-  if (B == 1) {
 #pragma unroll
-    for (int j = 0; j < MAXU_GU; ++j)
-      if (lane + kWave * j < UG) F::pack_x(xraw[j], xr[j]);
-  } else {
+  for (int q = 0; q < 2; ++q) {
+    const int i = threadIdx.x + q * kW * kWave;
+    if (i < B * UG) {
+      const int t = i / UG, u = i - (i / UG) * UG;
+      uint32_t xs[F::kXDw];
+      F::pack_x(xraw[q], xs);
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int i = threadIdx.x + q * kW * kWave;
-      if (i < B * UG) {
-        const int t = i / UG, u = i - (i / UG) * UG;
-        uint32_t xs[F::kXDw];
-        F::pack_x(xraw[q], xs);
-#pragma unroll
-        for (int c = 0; c < kCh; ++c)
-          xl[(t * kCh + c) * UG + u] = make_uint4(xs[4 * c], xs[4 * c + 1], xs[4 * c + 2], xs[4 * c + 3]);
-      }
+      for (int c = 0; c < kCh; ++c)
+        xl[(t * kCh + c) * UG + u] = make_uint4(xs[4 * c], xs[4 * c + 1], xs[4 * c + 2], xs[4 * c + 3]);
     }
   }
   if (threadIdx.x == 0) {
@@ -386,8 +414,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         wv[2 * i + 1] = lw[i];
         valid[2 * i] = valid[2 * i + 1] = lane + kWave * i < E;
       }
-      await_tags<2 * kPer>([&](int j) { return lg + ((int64_t)t * E + lane + kWave * (j >> 1)) * 2 + (j & 1); },
-                           wv, valid, tag, wall_clock64(), &s_timeout);
+      const int rr = await_tags<2 * kPer>(
+          [&](int j) { return lg + ((int64_t)t * E + lane + kWave * (j >> 1)) * 2 + (j & 1); }, wv, valid, tag,
+          wall_clock64(), &s_timeout);
+      if (a.trace && threadIdx.x == 0) trace_rereads = rr;
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
         hw[i] = wv[2 * i];
@@ -422,12 +452,27 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     cswap(0, 2);
     cswap(1, 3);
     cswap(1, 2);
+    // Each round: the largest head by the top 32 bits of its order-preserving
+    // key (one DPP max); when a single lane holds that key its head is the
+    // exact winner, else the tied lanes' heads are compared exactly.
     double my_v = 0.0;  // lane r keeps the rank-r selection
     int my_i = 0;
     for (int r = 0; r < k; ++r) {
-      double bv = v[0];
-      int bi = id[0];
-      wave_argmax(bv, bi);
+      const uint32_t key = order_key32(v[0] + 0.0);  // -0.0 compares equal to +0.0
+      const uint32_t top_key = wave_max_u32(key);
+      const uint64_t tied = __ballot(key == top_key);
+      double bv;
+      int bi;
+      if (__popcll(tied) == 1) {
+        const int L = (int)__builtin_ctzll(tied);
+        bv = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v[0]), L),
+                              __builtin_amdgcn_readlane(__double2loint(v[0]), L));
+        bi = __builtin_amdgcn_readlane(id[0], L);
+      } else {
+        bv = key == top_key ? v[0] : -__builtin_inf();
+        bi = key == top_key ? id[0] : 0x7FFFFFFF;
+        wave_argmax(bv, bi);
+      }
       if (lane == r) {
         my_v = bv;
         my_i = bi;
@@ -461,7 +506,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
   __syncthreads();
   stamp(a, 4);
-  // Group (token, rank) pairs by expert: experts ascending, tokens ascending.
+  // Group (token, rank) pairs by expert, experts ascending: one record per
+  // selected expert holding its packed token mask.
   if (w == 0) {
     int base = 0;
 #pragma unroll
@@ -469,24 +515,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       const int ex = q * kWave + lane;
       const uint32_t mask = ex < E ? s_mask[ex] : 0u;
       const uint64_t used = __ballot(mask != 0u);
-      if (mask != 0u) {
-        ExpertGroup* gr = &s_grp[base + __popcll(used & ((1ull << lane) - 1ull))];
-        gr->expert = ex;
-        gr->n = __popc(mask & 0xFFu);
-        int p = 0;
-#pragma unroll
-        for (int t = 0; t < kMaxTok; ++t) {
-          if ((mask >> t) & 1u) {
-            gr->tok[p] = t;
-            gr->slot[p] = (int)((mask >> (8 + 3 * t)) & 7u);
-            ++p;
-          }
-        }
-        for (; p < kMaxTok; ++p) {
-          gr->tok[p] = 0;
-          gr->slot[p] = 0;
-        }
-      }
+      if (mask != 0u) s_grp[base + __popcll(used & ((1ull << lane) - 1ull))] = LayerGroup{ex, mask};
       base += __popcll(used);
     }
     if (lane == 0) s_U = base;
@@ -506,89 +535,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   const int FS = Fd / NX;  // d_ff slice of this XCD
   const int f0 = xcd * FS;
   uint64_t* ht = reinterpret_cast<uint64_t*>(a.ws + a.L.h_tags);  // [S][Fd]
-  {
-    const int RPW = (FS + GX - 1) / GX;  // d_ff rows per workgroup
-    for (int r = w; r < RPW; r += kW) {
-      const int rl = jx * RPW + r;  // row inside the slice
-      if (rl >= FS) break;
-      const int row = f0 + rl;
-      typename F::Raw ring[kRingGU][2][MAXU_GU];
-      auto load_gu = [&](int uu, typename F::Raw(&dst)[2][MAXU_GU]) {
-        const bool live = uu < U;
-        const int ex = s_grp[live ? uu : U - 1].expert;
-        const uint16_t* gs = a.gate.scale ? reinterpret_cast<const uint16_t*>(
-                                                reinterpret_cast<const uint8_t*>(a.gate.scale) + ex * a.gate.scale_stride)
-                                          : nullptr;
-        const uint16_t* us = a.up.scale ? reinterpret_cast<const uint16_t*>(
-                                              reinterpret_cast<const uint8_t*>(a.up.scale) + ex * a.up.scale_stride)
-                                        : nullptr;
-        const typename F::Row rg = F::row(a.gate.base + ex * a.gate.stride, gs, row, D);
-        const typename F::Row ru = F::row(a.up.base + ex * a.up.stride, us, row, D);
-#pragma unroll
-        for (int j = 0; j < MAXU_GU; ++j) {
-          const int u = lane + kWave * j;
-          const int ul = (live && u < UG) ? u : 0;
-          F::load(rg, ul, dst[0][j]);
-          F::load(ru, ul, dst[1][j]);
-        }
-      };
-      auto compute_gu = [&](int uu, const typename F::Raw(&src)[2][MAXU_GU]) {
-        consume(src);
-        const int n = s_grp[uu].n;
-        for (int i = 0; i < n; ++i) {
-          const int t = s_grp[uu].tok[i];
-          float ag = 0.0f, au = 0.0f;
-#pragma unroll
-          for (int j = 0; j < MAXU_GU; ++j) {
-            const int u = lane + kWave * j;
-            if (u < UG) {
-              if (B == 1) {
-                ag += F::gu_dot(src[0][j], (uint32_t)u & 3u, xr[j]);
-                au += F::gu_dot(src[1][j], (uint32_t)u & 3u, xr[j]);
-              } else {
-                uint32_t xs[F::kXDw];
-#pragma unroll
-                for (int c = 0; c < kCh; ++c) {
-                  const uint4 p = xl[(t * kCh + c) * UG + u];
-                  xs[4 * c] = p.x;
-                  xs[4 * c + 1] = p.y;
-                  xs[4 * c + 2] = p.z;
-                  xs[4 * c + 3] = p.w;
-                }
-                ag += F::gu_dot(src[0][j], (uint32_t)u & 3u, xs);
-                au += F::gu_dot(src[1][j], (uint32_t)u & 3u, xs);
-              }
-            }
-          }
-          ag = wave_sum_dpp(ag);
-          au = wave_sum_dpp(au);
-          if (lane == 63) s_hv[w][t * k + s_grp[uu].slot[i]] = silu(ag) * au;
-        }
-      };
-#pragma unroll
-      for (int j = 0; j < kRingGU - 1; ++j) {
-        load_gu(j, ring[j]);
-        __builtin_amdgcn_sched_barrier(0);  // slots are requested in ring order
-      }
-      for (int base = 0; base < U; base += kRingGU) {
-#pragma unroll
-        for (int j = 0; j < kRingGU; ++j) {
-          load_gu(base + j + kRingGU - 1, ring[(j + kRingGU - 1) % kRingGU]);
-          __builtin_amdgcn_sched_barrier(0);
-          if (base + j < U)
-            compute_gu(base + j, ring[j]);
-          else
-            consume(ring[j]);
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      // Publish this row of h for every slot (each slot belongs to one group).
-      for (int s = lane; s < S; s += kWave) st_dev(ht + (int64_t)s * Fd + row, tagged(__float_as_uint(s_hv[w][s]), tag));
-    }
-  }
-  stamp(a, 6);
-
-  // ---------------------------------------------------------------- 3. down (partials over the slice)
+  // Down projection set-up.  The first experts' down weights are requested
+  // now, so they stream together with gate/up and are in registers when h
+  // arrives (at B=1 they are all of this workgroup's down weights).
   // LDS views: h slice per slot, unit blocks padded by 4 floats (conflict-free
   // float4 reads; Q2_K keeps its sub-block sums there), then the per-slot row
   // partials.
@@ -627,9 +576,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   };
   auto compute_dn = [&](int uu, const typename F::Raw(&src)[MAXU_DN]) {
     consume(src);
-    const int n = s_grp[uu].n;
-    for (int i = 0; i < n; ++i) {
-      const int s = s_grp[uu].tok[i] * k + s_grp[uu].slot[i];
+    const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_grp[uu].mask);
+    for (uint32_t m = mask & 0xFFu; m != 0u; m &= m - 1u) {  // tokens ascending
+      const int t = __builtin_ctz(m);
+      const int s = t * k + (int)((mask >> (8 + 3 * t)) & 7u);
       const float* hx = sh + (s * UPS + ub) * kHB;
 #pragma unroll
       for (int j = 0; j < MAXU_DN; ++j) {
@@ -642,13 +592,91 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       }
     }
   };
-  __syncthreads();  // the activation view of s_buf is no longer used
-  // The first experts' down weights are requested before waiting for h.
 #pragma unroll
   for (int j = 0; j < kRingDN - 1; ++j) {
     load_dn(j, dring[j]);
     __builtin_amdgcn_sched_barrier(0);  // slots are requested in ring order
   }
+  {
+    const int RPW = (FS + GX - 1) / GX;  // d_ff rows per workgroup
+    for (int r = w; r < RPW; r += kW) {
+      const int rl = jx * RPW + r;  // row inside the slice
+      if (rl >= FS) break;
+      const int row = f0 + rl;
+      typename F::Raw ring[kRingGU][2][MAXU_GU];
+      auto load_gu = [&](int uu, typename F::Raw(&dst)[2][MAXU_GU]) {
+        const bool live = uu < U;
+        const int ex = s_grp[live ? uu : U - 1].expert;
+        const uint16_t* gs = a.gate.scale ? reinterpret_cast<const uint16_t*>(
+                                                reinterpret_cast<const uint8_t*>(a.gate.scale) + ex * a.gate.scale_stride)
+                                          : nullptr;
+        const uint16_t* us = a.up.scale ? reinterpret_cast<const uint16_t*>(
+                                              reinterpret_cast<const uint8_t*>(a.up.scale) + ex * a.up.scale_stride)
+                                        : nullptr;
+        const typename F::Row rg = F::row(a.gate.base + ex * a.gate.stride, gs, row, D);
+        const typename F::Row ru = F::row(a.up.base + ex * a.up.stride, us, row, D);
+#pragma unroll
+        for (int j = 0; j < MAXU_GU; ++j) {
+          const int u = lane + kWave * j;
+          const int ul = (live && u < UG) ? u : 0;
+          F::load(rg, ul, dst[0][j]);
+          F::load(ru, ul, dst[1][j]);
+        }
+      };
+      auto compute_gu = [&](int uu, const typename F::Raw(&src)[2][MAXU_GU]) {
+        consume(src);
+        const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_grp[uu].mask);
+        for (uint32_t m = mask & 0xFFu; m != 0u; m &= m - 1u) {  // tokens ascending
+          const int t = __builtin_ctz(m);
+          float ag = 0.0f, au = 0.0f;
+#pragma unroll
+          for (int j = 0; j < MAXU_GU; ++j) {
+            const int u = lane + kWave * j;
+            if (u < UG) {
+              uint32_t xs[F::kXDw];
+#pragma unroll
+              for (int c = 0; c < kCh; ++c) {
+                const uint4 p = xl[(t * kCh + c) * UG + u];
+                xs[4 * c] = p.x;
+                xs[4 * c + 1] = p.y;
+                xs[4 * c + 2] = p.z;
+                xs[4 * c + 3] = p.w;
+              }
+              ag += F::gu_dot(src[0][j], (uint32_t)u & 3u, xs);
+              au += F::gu_dot(src[1][j], (uint32_t)u & 3u, xs);
+            }
+          }
+          ag = wave_sum_dpp(ag);
+          au = wave_sum_dpp(au);
+          if (lane == 63) s_hv[w][t * k + (int)((mask >> (8 + 3 * t)) & 7u)] = silu(ag) * au;
+        }
+      };
+#pragma unroll
+      for (int j = 0; j < kRingGU - 1; ++j) {
+        load_gu(j, ring[j]);
+        __builtin_amdgcn_sched_barrier(0);  // slots are requested in ring order
+      }
+      for (int base = 0; base < U; base += kRingGU) {
+#pragma unroll
+        for (int j = 0; j < kRingGU; ++j) {
+          load_gu(base + j + kRingGU - 1, ring[(j + kRingGU - 1) % kRingGU]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (base + j < U)
+            compute_gu(base + j, ring[j]);
+          else
+            consume(ring[j]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // Publish this row of h for every slot (each slot belongs to one group).
+      for (int s = lane; s < S; s += kWave) st_dev(ht + (int64_t)s * Fd + row, tagged(__float_as_uint(s_hv[w][s]), tag));
+    }
+  }
+  stamp(a, 6);
+
+  // ---------------------------------------------------------------- 3. down (partials over the slice)
+  __syncthreads();  // the activation view of s_buf is no longer used
+  stamp(a, 11);
   {
     // Gather this XCD's h slice for every slot (written by the XCD's workgroups).
     const uint64_t t0 = wall_clock64();
@@ -665,7 +693,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         valid[q] = i0 + q * kW * kWave < total;
         v[q] = valid[q] ? ld_xcd(hptr(q)) : 0ull;
       }
-      await_tags<kSpinBatch>(hptr, v, valid, tag, t0, &s_timeout);
+      const int rr = await_tags<kSpinBatch>(hptr, v, valid, tag, t0, &s_timeout);
+      trace_rereads += rr << 16;
 #pragma unroll
       for (int q = 0; q < kSpinBatch; ++q) {
         const int i = i0 + q * kW * kWave;
@@ -675,9 +704,13 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         }
       }
     }
+    stamp(a, 12);
+    if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints + 13] = (uint64_t)trace_rereads;
     __syncthreads();
-    for (int i = threadIdx.x; i < S * UPS; i += kW * kWave) F::prep_h(sh + i * kHB);
-    __syncthreads();
+    if (F::kPrepH) {
+      for (int i = threadIdx.x; i < S * UPS; i += kW * kWave) F::prep_h(sh + i * kHB);
+      __syncthreads();
+    }
   }
   stamp(a, 7);
   for (int base = 0; base < U; base += kRingDN) {

@@ -94,6 +94,7 @@ struct MxFmt {
     }
     return e8m0_to_f32(e) * acc;
   }
+  static constexpr bool kPrepH = false;
   static __device__ __forceinline__ void prep_h(float*) {}
   static __device__ __forceinline__ float dn_dot(const Raw& raw, uint32_t sh, const float* __restrict__ h) {
     return dot(raw, sh, h);
@@ -194,6 +195,7 @@ struct Q2kFmt {
     return acc;
   }
   // Sub-block sums of one unit's h (64 values) into h[64..67].
+  static constexpr bool kPrepH = true;
   static __device__ __forceinline__ void prep_h(float* h) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -320,6 +322,7 @@ struct Int4Fmt {
     return bf16_to_f32(raw.s) * __builtin_fmaf(acc, 512.0f, -8.0f * __uint_as_float(xs[16]));
   }
   // Sum of one unit's h (32 values) into h[32].
+  static constexpr bool kPrepH = true;
   static __device__ __forceinline__ void prep_h(float* h) {
     float sum = 0.0f;
 #pragma unroll
