@@ -36,6 +36,35 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+COUNTERS_MD = os.path.join(ROOT, "profiles", "fused_layer_mxfp4_hbm_counters.md")
+
+
+def kernel_source_sha256() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "quantized_moe_decode_route_amd", "csrc", "*"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per B=1 launch from the committed counter summary (rocprofv3
+    FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the kernel sources
+    changed after the counters were taken."""
+    try:
+        text = open(COUNTERS_MD).read()
+    except OSError:
+        return None
+    vals = dict(line.strip().split(": ", 1) for line in text.splitlines()
+                if line.strip().startswith(("traffic_b1_bytes:", "source_sha256:")))
+    if vals.get("source_sha256") != kernel_source_sha256():
+        return None
+    return int(vals["traffic_b1_bytes"])
+
+
 def build_layers(n_layers: int, seed: int, down_layout: str = "tile256"):
     """MXFP4 layers filled on the GPU from the seeded generator.  With
     down_layout "tile256" each expert's down projection is permuted once into
@@ -108,6 +137,29 @@ def profile_kernel(layers, xs, B, steps, warmup, ws):
     return float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]))
 
 
+COPY_BYTES = 256 << 20
+
+
+def counter_pass(layers, x1, x8, ws, n):
+    """Fixed launch order for per-dispatch hardware counters: n B=1 layers,
+    n B=8 layers, n plain device copies of COPY_BYTES (known traffic)."""
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    nl = len(layers)
+    for B, xs in ((1, x1), (8, x8)):
+        y = torch.empty((B, D), dtype=torch.float32, device="cuda")
+        for i in range(n):
+            moe.moe_layer_decode(layers[i % nl][0], xs[i], y, ws)
+        torch.cuda.synchronize()
+    src = torch.zeros(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        torch.neg(src, out=dst)  # one elementwise kernel: reads and writes COPY_BYTES each
+    torch.cuda.synchronize()
+    log(f"counter pass: {n} x B=1 layer, {n} x B=8 layer, {n} x elementwise copy of {COPY_BYTES} bytes")
+
+
 def cpu_baseline(seed: int, n_tokens: int):
     """The oracle on the host cores: B=1 layer decode for a few tokens."""
     import oracle
@@ -149,6 +201,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--down-layout", choices=("tile256", "rows"), default="tile256",
                     help="layout of the down projections (blocks permuted once at load time)")
+    ap.add_argument("--counter-pass", type=int, default=0, metavar="N",
+                    help="instead of the benchmark: N B=1 layer launches, then N B=8 launches, then N "
+                         "copies of a 256 MiB buffer (the copy calibrates HBM byte counters); for "
+                         "rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this decode path "
@@ -168,6 +224,10 @@ def main():
     x8 = [torch.from_numpy(synth.token_bf16(20000 + i, 8, D).view(np.int16)).to("cuda") for i in range(n_tok)]
     ws = torch.empty(moe.moe_layer_workspace_bytes(8, D, F, E, TOPK), dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(ws)
+
+    if args.counter_pass:
+        counter_pass(layers, x1, x8, ws, args.counter_pass)
+        return
 
     log("timing B=1 ...")
     ms1, wall1 = time_layer(layers, x1, 1, args.steps, args.warmup, ws)
@@ -213,7 +273,7 @@ def main():
         "kernel_ms": {"b1": round(k1, 5), "b8": round(k8, 5)},
         "roofline": {"kernel": "fused_layer_kernel (MXFP4, B=1)", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": bytes1,
+                     "traffic": measured_traffic(), "bytes_per_launch": bytes1,
                      "b8_achieved": round(bytes8 / (k8 * 1e-3) / 1e9, 2)},
     }
     if not args.no_cpu_baseline:

@@ -581,12 +581,25 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       const int t = __builtin_ctz(m);
       const int s = t * k + (int)((mask >> (8 + 3 * t)) & 7u);
       const float* hx = sh + (s * UPS + ub) * kHB;
+      // The lane's rows share one unit of h: read it from LDS once.
+      float hreg[kHB];
+      if (MAXU_DN > 1) {
+#pragma unroll
+        for (int c = 0; c < kHB / 4; ++c) {
+          const float4 v4 = *reinterpret_cast<const float4*>(hx + 4 * c);
+          hreg[4 * c] = v4.x;
+          hreg[4 * c + 1] = v4.y;
+          hreg[4 * c + 2] = v4.z;
+          hreg[4 * c + 3] = v4.w;
+        }
+      }
+      const float* hu = MAXU_DN > 1 ? hreg : hx;
 #pragma unroll
       for (int j = 0; j < MAXU_DN; ++j) {
         const int v = lane + kWave * j;
         const int rloc = w * RPV + v / UPS;
         const bool ok = v < UD && rloc < RPWd && n0 + rloc < D;
-        float pr = ok ? F::dn_dot(src[j], dsh, hx) : 0.0f;
+        float pr = ok ? F::dn_dot(src[j], dsh, hu) : 0.0f;
         pr = group_sum_dpp<UPS>(pr);
         if (ok && ub == 0) syp[s * RPWd + rloc] = pr;
       }
