@@ -202,8 +202,8 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID bits 3:0
 }
 
-__device__ __forceinline__ void stamp(const FusedArgs& a, int point) {
-  if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints + point] = wall_clock64();
+__device__ __forceinline__ void stamp(const FusedArgs& a, int point, unsigned by_thread = 0) {
+  if (a.trace && threadIdx.x == by_thread) a.trace[blockIdx.x * kTracePoints + point] = wall_clock64();
 }
 
 // Marks every dword of a ring slot as used here, on every path: the wave
@@ -356,8 +356,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       }
     }
     __syncthreads();
-    if (threadIdx.x < B) {
-      const int t = threadIdx.x;
+    // The last wave publishes (at B < 8 it gathers no token, so the other
+    // waves' reads of the logits do not wait behind these stores).
+    if (threadIdx.x >= (kW - 1) * kWave && threadIdx.x < (kW - 1) * kWave + B) {
+      const int t = threadIdx.x - (kW - 1) * kWave;
       double s = 0.0;
 #pragma unroll
       for (int i = 0; i < kW; ++i) s += s_part[i][t];
@@ -535,6 +537,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   const int FS = Fd / NX;  // d_ff slice of this XCD
   const int f0 = xcd * FS;
   uint64_t* ht = reinterpret_cast<uint64_t*>(a.ws + a.L.h_tags);  // [S][Fd]
+  const int RPW = (FS + GX - 1) / GX;  // d_ff rows per workgroup
   // Down projection set-up.  The first experts' down weights are requested
   // now, so they stream together with gate/up and are in registers when h
   // arrives (at B=1 they are all of this workgroup's down weights).
@@ -611,7 +614,6 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     __builtin_amdgcn_sched_barrier(0);  // slots are requested in ring order
   }
   {
-    const int RPW = (FS + GX - 1) / GX;  // d_ff rows per workgroup
     for (int r = w; r < RPW; r += kW) {
       const int rl = jx * RPW + r;  // row inside the slice
       if (rl >= FS) break;
@@ -692,25 +694,26 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   stamp(a, 11);
   {
     // Gather this XCD's h slice for every slot (written by the XCD's workgroups).
+    const int g_first = threadIdx.x, g_step = kW * kWave;
     const uint64_t t0 = wall_clock64();
     const int total = S * FS;
-    for (int i0 = threadIdx.x; i0 < total; i0 += kSpinBatch * kW * kWave) {
+    for (int i0 = g_first; i0 < total; i0 += kSpinBatch * g_step) {
       auto hptr = [&](int q) {
-        const int i = i0 + q * kW * kWave;
+        const int i = i0 + q * g_step;
         return ht + (int64_t)(i / FS) * Fd + f0 + (i - (i / FS) * FS);
       };
       uint64_t v[kSpinBatch];
       bool valid[kSpinBatch];
 #pragma unroll
       for (int q = 0; q < kSpinBatch; ++q) {
-        valid[q] = i0 + q * kW * kWave < total;
+        valid[q] = i0 + q * g_step < total;
         v[q] = valid[q] ? ld_xcd(hptr(q)) : 0ull;
       }
       const int rr = await_tags<kSpinBatch>(hptr, v, valid, tag, t0, &s_timeout);
       trace_rereads += rr << 16;
 #pragma unroll
       for (int q = 0; q < kSpinBatch; ++q) {
-        const int i = i0 + q * kW * kWave;
+        const int i = i0 + q * g_step;
         if (valid[q]) {
           const int s = i / FS, f = i - (i / FS) * FS;
           sh[(s * UPS + f / F::kUnitW) * kHB + f % F::kUnitW] = __uint_as_float(payload_of(v[q]));
@@ -739,10 +742,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
   __syncthreads();
   stamp(a, 8);
-  // Combine the k ranks in rank order and publish this XCD's partial rows.
-  {
+  // Combine the k ranks in rank order and publish this XCD's partial rows
+  // (first half of the waves), while the second half gathers the partials of
+  // the rows this workgroup finishes.
+  if (w < kW / 2) {
     uint64_t* pt = reinterpret_cast<uint64_t*>(a.ws + a.L.part_tags);  // [NX][B][D]
-    for (int i = threadIdx.x; i < B * RPWd; i += blockDim.x) {
+    for (int i = threadIdx.x; i < B * RPWd; i += (kW / 2) * kWave) {
       const int t = i / RPWd, rl = i - (i / RPWd) * RPWd;
       const int n = n0 + rl;
       if (n < D) {
@@ -755,12 +760,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   stamp(a, 9);
 
   // ---------------------------------------------------------------- finish: sum the NX partials
-  {
+  if (w >= kW / 2) {
     const uint64_t* pt = reinterpret_cast<const uint64_t*>(a.ws + a.L.part_tags);
     const int RF = (RPWd + NX - 1) / NX;  // rows this workgroup finishes
     const int rf0 = xcd * RF;
     const uint64_t t0 = wall_clock64();
-    for (int i = threadIdx.x; i < B * RF; i += blockDim.x) {
+    for (int i = threadIdx.x - (kW / 2) * kWave; i < B * RF; i += (kW / 2) * kWave) {
       const int t = i / RF, rl = rf0 + (i - (i / RF) * RF);
       const int n = n0 + rl;
       if (rl < RPWd && n < D) {
