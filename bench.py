@@ -96,6 +96,158 @@ def build_layers(n_layers: int, seed: int, down_layout: str = "tile256"):
     return layers
 
 
+Q2K_MAT = F * (D // 256) * 84        # 2,752,512 bytes per projection (gate/up [F][D] and down [D][F])
+I4_Q = F * D // 2                    # INT4 codes per projection
+I4_S = F * (D // 32) * 2             # bfloat16 scales per projection
+EXPERT_BYTES = {"mxfp4": 3 * MX_MAT, "q2k": 3 * Q2K_MAT, "int4g32": 3 * (I4_Q + I4_S)}
+
+
+def build_format_layers(fmt: str, n_layers: int, seed: int):
+    """Layers of `fmt` with 256-column tiled down projections: Q2_K filled on
+    the GPU from the seeded generator; INT4 converted on the GPU from seeded
+    MXFP4 experts by quantize_fp4_to_int4g32."""
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    import synth
+    if fmt == "mxfp4":
+        return build_layers(n_layers, seed, "tile256")
+    stream = torch.cuda.current_stream().cuda_stream
+    layers = []
+    if fmt == "q2k":
+        tmp = torch.empty(E * Q2K_MAT, dtype=torch.uint8, device="cuda")
+        for l in range(n_layers):
+            mats = []
+            for proj in (synth.PROJ_GATE, synth.PROJ_UP, synth.PROJ_DOWN):
+                buf = torch.empty(E * Q2K_MAT, dtype=torch.uint8, device="cuda")
+                dst = tmp if proj == synth.PROJ_DOWN else buf
+                synth.gpu_fill("q2k", dst.data_ptr(), seed, l, 0, E, proj, F * D // 256, stream)
+                if proj == synth.PROJ_DOWN:
+                    for e in range(E):
+                        moe.moe_tile_weights("q2k", tmp.data_ptr() + e * Q2K_MAT, D, F, buf.data_ptr() + e * Q2K_MAT)
+                mats.append(buf)
+            router = torch.from_numpy(synth.router_weights(seed, l, E, D)).to("cuda")
+            desc = moe.make_layer_desc("q2k", router, mats[0], mats[1], mats[2], E, D, F, TOPK,
+                                       Q2K_MAT, Q2K_MAT, Q2K_MAT, down_layout="tile256")
+            layers.append((desc, mats, router))
+    else:
+        mx = torch.empty(E * MX_MAT, dtype=torch.uint8, device="cuda")
+        tq = torch.empty(I4_Q, dtype=torch.uint8, device="cuda")
+        ts = torch.empty(I4_S, dtype=torch.uint8, device="cuda")
+        for l in range(n_layers):
+            mats = []
+            for proj, (n, kk) in ((synth.PROJ_GATE, (F, D)), (synth.PROJ_UP, (F, D)), (synth.PROJ_DOWN, (D, F))):
+                synth.gpu_fill("mxfp4", mx.data_ptr(), seed, l, 0, E, proj, F * D // 32, stream)
+                q = torch.empty(E * I4_Q, dtype=torch.uint8, device="cuda")
+                sc = torch.empty(E * I4_S, dtype=torch.uint8, device="cuda")
+                for e in range(E):
+                    if proj == synth.PROJ_DOWN:
+                        moe.quantize_fp4_to_int4g32(mx.data_ptr() + e * MX_MAT, n, kk, tq.data_ptr(), ts.data_ptr())
+                        moe.moe_tile_weights("int4g32", tq.data_ptr(), n, kk, q.data_ptr() + e * I4_Q,
+                                             src_scale=ts.data_ptr(), dst_scale=sc.data_ptr() + e * I4_S)
+                    else:
+                        moe.quantize_fp4_to_int4g32(mx.data_ptr() + e * MX_MAT, n, kk, q.data_ptr() + e * I4_Q,
+                                                    sc.data_ptr() + e * I4_S)
+                mats += [q, sc]
+            router = torch.from_numpy(synth.router_weights(seed, l, E, D)).to("cuda")
+            desc = moe.make_layer_desc("int4g32", router, mats[0], mats[2], mats[4], E, D, F, TOPK,
+                                       I4_Q, I4_Q, I4_Q, mats[1], mats[3], mats[5], I4_S, I4_S, I4_S,
+                                       down_layout="tile256")
+            layers.append((desc, mats, router))
+    torch.cuda.synchronize()
+    return layers
+
+
+def format_leg(fmt: str, n_layers: int, seed: int, steps: int, warmup: int, ws):
+    """B=1 and B=8 layer throughput for one weight format (effective weight GB/s)."""
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    import synth
+    log(f"{fmt}: building {n_layers} layers ...")
+    layers = build_format_layers(fmt, n_layers, seed)
+    out = {}
+    for B in (1, 8):
+        xs = [torch.from_numpy(synth.token_bf16(50000 + 97 * B + i, B, D).view(np.int16)).to("cuda")
+              for i in range(warmup + steps)]
+        idx_log = torch.empty((steps, B, TOPK), dtype=torch.int32, device="cuda")
+        ms, _ = time_layer(layers, xs, B, steps, warmup, ws, idx_log)
+        U = float(np.mean([len(np.unique(r)) for r in idx_log.cpu().numpy()]))
+        nbytes = U * EXPERT_BYTES[fmt] + ROUTER
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"b{B}"] = {"value": round(gbs, 2), "unit": "GB/s", "ms_per_step": round(ms, 5),
+                        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                        "tokens_per_s_layer": round(B * 1e3 / ms, 1), "mean_unique_experts": round(U, 2),
+                        "bytes_per_step": round(nbytes)}
+    del layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def stack_leg(n_layers: int, seed: int, steps: int, warmup: int, mean_u8: float):
+    """The residual stream through n_layers resident MXFP4 layers (moe_stack_decode)."""
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    import synth
+    log(f"stack: building {n_layers} MXFP4 layers ({n_layers * 3 * E * MX_MAT / 1e9:.0f} GB resident) ...")
+    layers = build_layers(n_layers, seed, "tile256")
+    descs = [l[0] for l in layers]
+    ws = torch.empty(moe.moe_stack_workspace_bytes(8, D, F, E, TOPK), dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws)
+    out = {"layers": n_layers, "resident_bytes": n_layers * (3 * E * MX_MAT + ROUTER)}
+    for B in (1, 8):
+        hs = [torch.from_numpy(synth.token_f32(70000 + 31 * B + i, B, D)).to("cuda") for i in range(warmup + steps)]
+        hout = torch.empty((B, D), dtype=torch.float32, device="cuda")
+        for i in range(warmup):
+            moe.moe_stack_decode(descs, hs[i], hout, ws)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            moe.moe_stack_decode(descs, hs[warmup + i], hout, ws)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / steps
+        u = TOPK if B == 1 else mean_u8
+        nbytes = n_layers * (u * EXPERT_BYTES["mxfp4"] + ROUTER)
+        out[f"b{B}"] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * 1e3 / ms, 1),
+                        "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+                        "bytes_per_step": round(nbytes),
+                        "bytes_note": "exact" if B == 1 else "mean unique experts per layer taken from the B=8 layer leg"}
+    del layers, descs
+    torch.cuda.empty_cache()
+    return out
+
+
+def gemv_leg(steps: int, warmup: int, copies: int = 128):
+    """Stand-alone MXFP4 matvec W [2048 x 4096] x fp32 x, rotated over `copies` matrices."""
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    import synth
+    stream = torch.cuda.current_stream().cuda_stream
+    w = torch.empty(copies * MX_MAT, dtype=torch.uint8, device="cuda")
+    synth.gpu_fill("mxfp4", w.data_ptr(), 0x5EED + 9, 0, 0, copies, synth.PROJ_GATE, F * D // 32, stream)
+    x = torch.from_numpy(synth.token_f32(90000, 1, D)).to("cuda")
+    y = torch.empty((1, F), dtype=torch.float32, device="cuda")
+    for i in range(warmup):
+        moe.moe_expert_gemv_mxfp4(w.data_ptr() + (i % copies) * MX_MAT, F, D, x, y)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        moe.moe_expert_gemv_mxfp4(w.data_ptr() + ((warmup + i) % copies) * MX_MAT, F, D, x, y)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    del w
+    torch.cuda.empty_cache()
+    gbs = MX_MAT / (ms * 1e-3) / 1e9
+    return {"value": round(gbs, 2), "unit": "GB/s", "us_per_call": round(ms * 1e3, 3),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "bytes_per_call": MX_MAT, "copies_rotated": copies}
+
+
 def time_layer(layers, xs, B, steps, warmup, ws, idx_log=None):
     import torch
 
@@ -201,6 +353,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--down-layout", choices=("tile256", "rows"), default="tile256",
                     help="layout of the down projections (blocks permuted once at load time)")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the headline MXFP4 layer (skip the Q2_K, INT4, 43-layer stack and matvec legs)")
+    ap.add_argument("--stack-layers", type=int, default=43)
     ap.add_argument("--counter-pass", type=int, default=0, metavar="N",
                     help="instead of the benchmark: N B=1 layer launches, then N B=8 launches, then N "
                          "copies of a 256 MiB buffer (the copy calibrates HBM byte counters); for "
@@ -276,6 +431,14 @@ def main():
                      "traffic": measured_traffic(), "bytes_per_launch": bytes1,
                      "b8_achieved": round(bytes8 / (k8 * 1e-3) / 1e9, 2)},
     }
+    if not args.no_extra:
+        del layers
+        torch.cuda.empty_cache()
+        ext_steps, ext_warm = max(args.steps // 2, 10), max(args.warmup // 2, 5)
+        result["formats"] = {f: format_leg(f, 4, args.seed + 7, ext_steps, ext_warm, ws) for f in ("q2k", "int4g32")}
+        result["stack"] = stack_leg(args.stack_layers, args.seed + 11, 10, 2, U8)
+        log("matvec ...")
+        result["gemv_mxfp4_2048x4096"] = gemv_leg(args.steps, args.warmup)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_tokens)
