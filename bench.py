@@ -65,17 +65,18 @@ def measured_traffic():
     return int(vals["traffic_b1_bytes"])
 
 
-def build_layers(n_layers: int, seed: int, down_layout: str = "tile256"):
+def build_layers(n_layers: int, seed: int, down_layout: str = "mfma16"):
     """MXFP4 layers filled on the GPU from the seeded generator.  With
-    down_layout "tile256" each expert's down projection is permuted once into
-    the 256-column tiled layout (moe_tile_weights), as a loader would."""
+    down_layout "tile256" or "mfma16" each expert's down projection is
+    permuted once into that layout (moe_tile_weights / _mfma16), as a loader
+    would."""
     import torch
 
     import quantized_moe_decode_route_amd as moe
     import synth
     stream = torch.cuda.current_stream().cuda_stream
     layers = []
-    tmp = torch.empty(E * MX_MAT, dtype=torch.uint8, device="cuda") if down_layout == "tile256" else None
+    tmp = torch.empty(E * MX_MAT, dtype=torch.uint8, device="cuda") if down_layout != "rows" else None
     for l in range(n_layers):
         mats = []
         for proj in (synth.PROJ_GATE, synth.PROJ_UP, synth.PROJ_DOWN):
@@ -83,7 +84,10 @@ def build_layers(n_layers: int, seed: int, down_layout: str = "tile256"):
             if proj == synth.PROJ_DOWN and tmp is not None:
                 synth.gpu_fill("mxfp4", tmp.data_ptr(), seed, l, 0, E, proj, F * D // 32, stream)
                 for e in range(E):
-                    moe.moe_tile_weights("mxfp4", tmp.data_ptr() + e * MX_MAT, D, F, buf.data_ptr() + e * MX_MAT)
+                    if down_layout == "tile256":
+                        moe.moe_tile_weights("mxfp4", tmp.data_ptr() + e * MX_MAT, D, F, buf.data_ptr() + e * MX_MAT)
+                    else:
+                        moe.moe_tile_weights_mfma16(tmp.data_ptr() + e * MX_MAT, D, F, buf.data_ptr() + e * MX_MAT)
             else:
                 synth.gpu_fill("mxfp4", buf.data_ptr(), seed, l, 0, E, proj, F * D // 32, stream)
             mats.append(buf)
@@ -111,7 +115,7 @@ def build_format_layers(fmt: str, n_layers: int, seed: int):
     import quantized_moe_decode_route_amd as moe
     import synth
     if fmt == "mxfp4":
-        return build_layers(n_layers, seed, "tile256")
+        return build_layers(n_layers, seed, "mfma16")
     stream = torch.cuda.current_stream().cuda_stream
     layers = []
     if fmt == "q2k":
@@ -191,7 +195,7 @@ def stack_leg(n_layers: int, seed: int, steps: int, warmup: int, mean_u8: float)
     import quantized_moe_decode_route_amd as moe
     import synth
     log(f"stack: building {n_layers} MXFP4 layers ({n_layers * 3 * E * MX_MAT / 1e9:.0f} GB resident) ...")
-    layers = build_layers(n_layers, seed, "tile256")
+    layers = build_layers(n_layers, seed, "mfma16")
     descs = [l[0] for l in layers]
     ws = torch.empty(moe.moe_stack_workspace_bytes(8, D, F, E, TOPK), dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(ws)
@@ -351,7 +355,7 @@ def main():
     ap.add_argument("--seed", type=int, default=0x5EED + 1)
     ap.add_argument("--cpu-tokens", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--down-layout", choices=("tile256", "rows"), default="tile256",
+    ap.add_argument("--down-layout", choices=("mfma16", "tile256", "rows"), default="mfma16",
                     help="layout of the down projections (blocks permuted once at load time)")
     ap.add_argument("--no-extra", action="store_true",
                     help="only the headline MXFP4 layer (skip the Q2_K, INT4, 43-layer stack and matvec legs)")

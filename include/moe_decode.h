@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 enum moe_status {
   MOE_OK = 0,
@@ -70,8 +70,19 @@ enum moe_format { MOE_FMT_MXFP4 = 0, MOE_FMT_Q2K = 1, MOE_FMT_INT4G32 = 2 };
  *                       [(K/256) * N][256] matrix whose row c*N + n holds
  *                       columns 256c .. 256c+255 of row n.  A decode kernel
  *                       that splits K over the chip's XCDs then reads one
- *                       contiguous region per XCD.  K % 256 == 0. */
-enum moe_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILE256 = 1 };
+ *                       contiguous region per XCD.  K % 256 == 0.
+ *   MOE_LAYOUT_MFMA16   MXFP4 only: the TILE256 order refined for the
+ *                       16x16x128 matrix-core operation.  Inside each tile
+ *                       the rows are taken 16 at a time, and the 16 x 8
+ *                       blocks of such a group are stored as 2 halves (tile
+ *                       columns 0..127, 128..255) x 4 quarters (32 columns
+ *                       each) x 16 rows: block j of row n, j = 8c + 4h + q,
+ *                       is block number
+ *                         (((c * N/16 + n/16) * 2 + h) * 4 + q) * 16 + n%16
+ *                       of the matrix.  One 64-lane load of 17-byte blocks
+ *                       then fetches a whole 16-row x 128-column operand from
+ *                       contiguous memory.  N % 16 == 0, K % 256 == 0. */
+enum moe_layout { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILE256 = 1, MOE_LAYOUT_MFMA16 = 2 };
 
 #define MOE_MAX_TOKENS 8   /* B: one token plus up to 7 speculative drafts */
 #define MOE_MAX_TOPK 8
@@ -223,6 +234,9 @@ int quantize_fp4_to_int4g32(const uint8_t* mxfp4, int N, int K, int32_t* q_out, 
  * Returns MOE_ERR_SHAPE / _ALIGN / _ARG on bad arguments, before any work. */
 int moe_tile_weights(int format, const void* src, const uint16_t* src_scale, int N, int K, void* dst,
                      uint16_t* dst_scale, void* stream);
+/* Same for MXFP4 blocks [N][K/32][17] into MOE_LAYOUT_MFMA16 (dst).  N % 16
+ * == 0 and K % 256 == 0 (MOE_ERR_SHAPE); src and dst do not overlap. */
+int moe_tile_weights_mfma16(const uint8_t* src, int N, int K, uint8_t* dst, void* stream);
 
 /* Count MXFP4 blocks whose exponent byte is 0xFF (scale +inf: infinity times
  * a zero code is NaN, which the ds4 notes treat as an error for E8M0 scales).

@@ -17,8 +17,10 @@ LIB_PATH = os.path.join(PKG_DIR, "libmoedecode.so")
 MOE_OK = 0
 MOE_FMT_MXFP4, MOE_FMT_Q2K, MOE_FMT_INT4G32 = 0, 1, 2
 FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2k": MOE_FMT_Q2K, "int4g32": MOE_FMT_INT4G32}
-MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE256 = 0, 1
-LAYOUTS = {"rows": MOE_LAYOUT_ROWS, "tile256": MOE_LAYOUT_TILE256}
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE256, MOE_LAYOUT_MFMA16 = 0, 1, 2
+LAYOUTS = {"rows": MOE_LAYOUT_ROWS, "tile256": MOE_LAYOUT_TILE256, "mfma16": MOE_LAYOUT_MFMA16}
+# MOE_ABI_VERSION of include/moe_decode.h that this binding is written for
+ABI_VERSION = 3
 MOE_MAX_TOKENS = 8
 MOE_MAX_TOPK = 8
 
@@ -29,7 +31,7 @@ EXPORTS = (
     "moe_layer_workspace_bytes", "moe_workspace_init", "moe_layer_decode", "moe_layer_decode_profiled",
     "moe_layer_decode_traced",
     "moe_stack_workspace_bytes", "moe_stack_decode", "moe_rmsnorm_bf16",
-    "quantize_fp4_to_int4g32", "moe_validate_mxfp4", "moe_tile_weights",
+    "quantize_fp4_to_int4g32", "moe_validate_mxfp4", "moe_tile_weights", "moe_tile_weights_mfma16",
 )
 
 
@@ -90,6 +92,7 @@ def lib() -> ctypes.CDLL:
             "quantize_fp4_to_int4g32": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
             "moe_validate_mxfp4": (_i, [_vp, _i64, _vp, _vp]),
             "moe_tile_weights": (_i, [_i, _vp, _vp, _i, _i, _vp, _vp, _vp]),
+            "moe_tile_weights_mfma16": (_i, [_vp, _i, _i, _vp, _vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -181,7 +184,8 @@ def make_layer_desc(fmt: str, router_w, gate, up, down, n_experts: int, d_model:
                     down_scale=None, gate_scale_stride: int = 0, up_scale_stride: int = 0,
                     down_scale_stride: int = 0, down_layout: str = "rows") -> moe_layer_desc:
     """Fill the C descriptor; tensors (or raw device addresses) must outlive its use.
-    ``down_layout``: "rows" (as published) or "tile256" (see moe_tile_weights)."""
+    ``down_layout``: "rows" (as published), "tile256" (see moe_tile_weights) or
+    "mfma16" (MXFP4 only, see moe_tile_weights_mfma16)."""
     d = moe_layer_desc()
     d.format = FORMATS[fmt]
     d.n_experts, d.d_model, d.d_ff, d.top_k = n_experts, d_model, d_ff, top_k
@@ -263,6 +267,11 @@ def moe_tile_weights(fmt: str, src, N: int, K: int, dst, src_scale=None, dst_sca
     _check("moe_tile_weights",
            lib().moe_tile_weights(FORMATS[fmt], _ptr(src), _ptr(src_scale), N, K, _ptr(dst), _ptr(dst_scale),
                                   _stream(stream)))
+
+
+def moe_tile_weights_mfma16(src, N: int, K: int, dst, stream=None) -> None:
+    """Row-major MXFP4 [N][K] blocks -> MOE_LAYOUT_MFMA16 (a block permutation)."""
+    _check("moe_tile_weights_mfma16", lib().moe_tile_weights_mfma16(_ptr(src), N, K, _ptr(dst), _stream(stream)))
 
 
 def moe_validate_mxfp4(blocks, n_blocks: int, bad_count_dev, stream=None) -> None:

@@ -59,8 +59,12 @@ int check_layer(const moe_layer_desc* L, int B) {
   const uintptr_t wa = L->format == MOE_FMT_INT4G32 ? 16 : 4;
   if (!aligned(L->gate, wa) || !aligned(L->up, wa) || !aligned(L->down, wa)) return MOE_ERR_ALIGN;
   if (L->gate_stride % wa || L->up_stride % wa || L->down_stride % wa) return MOE_ERR_ALIGN;
-  if (L->down_layout != MOE_LAYOUT_ROWS && L->down_layout != MOE_LAYOUT_TILE256) return MOE_ERR_ARG;
-  if (L->down_layout == MOE_LAYOUT_TILE256 && L->d_ff % kTileCols) return MOE_ERR_SHAPE;
+  if (L->down_layout != MOE_LAYOUT_ROWS && L->down_layout != MOE_LAYOUT_TILE256 &&
+      L->down_layout != MOE_LAYOUT_MFMA16)
+    return MOE_ERR_ARG;
+  if (L->down_layout == MOE_LAYOUT_MFMA16 && L->format != MOE_FMT_MXFP4) return MOE_ERR_ARG;
+  if (L->down_layout != MOE_LAYOUT_ROWS && L->d_ff % kTileCols) return MOE_ERR_SHAPE;
+  if (L->down_layout == MOE_LAYOUT_MFMA16 && L->d_model % 16) return MOE_ERR_SHAPE;
   if (L->format == MOE_FMT_INT4G32) {
     if (!L->gate_scale || !L->up_scale || !L->down_scale) return MOE_ERR_ARG;
     if (!aligned(L->gate_scale, 2) || !aligned(L->up_scale, 2) || !aligned(L->down_scale, 2)) return MOE_ERR_ALIGN;
@@ -75,7 +79,7 @@ WeightRef wref(const void* base, int64_t stride, const uint16_t* scale, int64_t 
   w.stride = stride;
   w.scale = scale;
   w.scale_stride = scale_stride;
-  w.tiled = layout == MOE_LAYOUT_TILE256 ? 1 : 0;
+  w.layout = layout;
   return w;
 }
 
@@ -96,7 +100,7 @@ int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
   const int grid = fused_grid_size();
   int nx = xcd_count();
   if (nx == 0) nx = probe_xcd_count(reinterpret_cast<uint32_t*>(w + W.topo), grid, s);
-  if (nx > 0 && fused_shape(L->format, B, k, D, F, grid, nx).ok) {
+  if (nx > 0 && fused_shape(L->format, B, k, D, F, grid, nx, L->down_layout).ok) {
     e = launch_fused_layer(L->format, L->router_w, x_bf16, g, u, d, E, D, F, k, B, w, W, y, residual, idx_out,
                            gw_out, trace, s);
     if (e != hipSuccess) return hip_status(e);
@@ -240,7 +244,7 @@ int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int
   if ((st = arch_check()) != MOE_OK) return st;
   const int grid = fused_grid_size();
   const int nx = xcd_count();
-  const bool fused = nx > 0 && fused_shape(L->format, B, L->top_k, L->d_model, L->d_ff, grid, nx).ok;
+  const bool fused = nx > 0 && fused_shape(L->format, B, L->top_k, L->d_model, L->d_ff, grid, nx, L->down_layout).ok;
   *trace_blocks = fused ? grid : 0;
   if (!trace) return MOE_OK;  // size query
   return layer_impl(L, x_bf16, B, y, nullptr, ws, nullptr, nullptr, nullptr, (hipStream_t)stream, trace);
@@ -321,6 +325,14 @@ int moe_tile_weights(int format, const void* src, const uint16_t* src_scale, int
   hipError_t e = launch_tile_rows(src, dst, N, tiles, tile_bytes / 4, 4, s);
   if (e == hipSuccess && int4) e = launch_tile_rows(src_scale, dst_scale, N, tiles, kTileCols / 32, 2, s);
   return hip_status(e);
+}
+
+int moe_tile_weights_mfma16(const uint8_t* src, int N, int K, uint8_t* dst, void* stream) {
+  if (!src || !dst || N <= 0 || K <= 0) return MOE_ERR_ARG;
+  if (K % kTileCols || N % 16) return MOE_ERR_SHAPE;
+  int st = arch_check();
+  if (st != MOE_OK) return st;
+  return hip_status(launch_tile_mfma16(src, dst, N, K, (hipStream_t)stream));
 }
 
 int moe_validate_mxfp4(const uint8_t* blocks, int64_t n_blocks, int32_t* bad_count_dev, void* stream) {

@@ -22,9 +22,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void xcc_map_kernel(uint32_t* out) {
 
 }  // namespace
 
-FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx) {
+FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx, int down_layout) {
   FusedShape sh{};
   sh.ok = false;
+  sh.mfma = down_layout == MOE_LAYOUT_MFMA16;
+  if (sh.mfma && fmt != MOE_FMT_MXFP4) return sh;
   if (grid <= 0 || nx <= 0 || nx > kMaxNX || grid % nx) return sh;
   const int uw = fmt == MOE_FMT_Q2K ? 64 : 32;
   const int gx = grid / nx;
@@ -41,7 +43,15 @@ FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx) {
   // LDS: activations during gate/up, then h slices and row partials.
   const size_t staged = fmt == MOE_FMT_Q2K ? 4 * Q2kFmt::kXDw : fmt == MOE_FMT_INT4G32 ? 4 * Int4Fmt::kXDw : 4 * MxFmt::kXDw;
   const size_t act = (size_t)B * (D / uw) * staged;
-  const size_t down = (size_t)B * k * ups * (uw + 4) * 4 + (size_t)B * k * rpwd * 4;
+  size_t down = (size_t)B * k * ups * (uw + 4) * 4 + (size_t)B * k * rpwd * 4;
+  if (sh.mfma) {
+    // one 16-row tile per wave, at most two 128-column k-steps per XCD
+    // slice; the B operands and row partials sit beside the activations
+    if (rpv > 16 || ups > 8) return sh;
+    const size_t S = (size_t)B * k, dnk = (ups + 3) / 4;
+    auto up16 = [](size_t v) { return (v + 15) & ~(size_t)15; };
+    down = up16(act) + (S + 1) * dnk * 512 + up16((S + 1) * 4 * dnk) + S * rpwd * 4;
+  }
   if (act > (size_t)kLdsBytes || down > (size_t)kLdsBytes) return sh;
   sh.ok = true;
   return sh;
@@ -119,8 +129,9 @@ hipError_t launch_fused_layer(int fmt, const float* router_w, const uint16_t* x,
   a.B = B;
   a.nx = xcd_count();
   const int grid = fused_grid_size();
-  const FusedShape sh = fused_shape(fmt, B, k, D, Fd, grid, a.nx);
+  const FusedShape sh = fused_shape(fmt, B, k, D, Fd, grid, a.nx, down.layout);
   if (!sh.ok) return hipErrorInvalidValue;
+  if (sh.mfma) return fused::launch_mx_mfma(a, grid, sh.gu_units, sh.ups, s);
   switch (fmt) {
     case MOE_FMT_MXFP4: return fused::launch_mx(a, grid, sh.gu_units, sh.dn_units, sh.ups, s);
     case MOE_FMT_Q2K: return fused::launch_q2k(a, grid, sh.gu_units, sh.dn_units, sh.ups, s);

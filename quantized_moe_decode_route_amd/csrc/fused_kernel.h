@@ -246,8 +246,8 @@ __device__ __forceinline__ int await_tags(Addr addr, uint64_t (&v)[N], const boo
 }
 
 // LDS shared by the phases (activations during gate/up; h slices and row
-// partials during down).
-constexpr int kLdsBytes = 128 * 1024;
+// partials during down; on the matrix-core path both at once).
+constexpr int kLdsBytes = 140 * 1024;
 // Experts whose weights a wave has in flight or in use: the loads for expert
 // uu + R - 1 are issued before expert uu is computed.  The rings are indexed
 // with compile-time constants only (no register copies, which would make the
@@ -266,7 +266,7 @@ struct Rings<Int4Fmt> {  // its gate/up unpacking keeps more registers live
 };
 constexpr int kSpinBatch = 12;  // tagged words a thread reads before its first wait
 
-template <class F, int MAXU_GU, int MAXU_DN, int UPS>
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK>
 __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a) {
   constexpr int kCh = F::kXDw / 4;  // 16-byte chunks of one unit's staged activations
   constexpr int kRingGU = Rings<F>::kGU;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   __shared__ LayerGroup s_grp[kMaxSlots];
   __shared__ uint32_t s_mask[MOE_MAX_EXPERTS];  // per expert: tokens that picked it and at which rank
   __shared__ double s_part[kW][kMaxTok];
-  __shared__ float s_hv[kW][kMaxSlots];  // a wave's h values for its current row, per slot
+  __shared__ int s_next;                 // matrix-core path: next token slot to gather
   __shared__ int s_U;
   __shared__ int s_timeout;
   __shared__ int s_jx;
@@ -307,6 +307,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
                                          __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   for (int i = threadIdx.x; i < MOE_MAX_EXPERTS; i += blockDim.x) s_mask[i] = 0u;
+  if (threadIdx.x == 0) s_next = 0;
 
   // Activations for gate/up: requested now, staged in LDS ([t][chunk][unit],
   // so lanes read consecutive chunks) after the router logits.  B * units <=
@@ -522,8 +523,50 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
     if (lane == 0) s_U = base;
   }
+  if constexpr (DNK > 0) {  // the zero B operand (slot S) read by lanes without a token
+    uint8_t* hb0 = s_buf + (((size_t)B * UG * kCh * 16 + 15) & ~(size_t)15);
+    for (int i = threadIdx.x; i < DNK * 512 / 16; i += kW * kWave)
+      reinterpret_cast<uint4*>(hb0 + (size_t)S * DNK * 512)[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x < 4 * DNK) hb0[(size_t)(S + 1) * DNK * 512 + S * 4 * DNK + threadIdx.x] = 0;
+  }
   __syncthreads();
   const int U = s_U;
+  // The group table, one group per lane (U <= kMaxSlots = 64): the rings read
+  // an expert or a token mask with v_readlane instead of an LDS round trip.
+  // For the matrix-core down projection, the slots of the group's tokens in
+  // ascending token order, one byte each (tokens 0..3 in gsl_lo, 4..7 in
+  // gsl_hi).
+  static_assert(kMaxSlots <= kWave, "one group per lane");
+  int g_exp;
+  uint32_t g_mask, gsl_lo = 0u, gsl_hi = 0u;
+  {
+    const LayerGroup gr = s_grp[min(lane, U - 1)];
+    g_exp = gr.expert;
+    g_mask = gr.mask;
+    uint32_t m = g_mask & 0xFFu;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = m ? __builtin_ctz(m) : 0;
+      const uint32_t sl = m ? (uint32_t)(t * k + (int)((g_mask >> (8 + 3 * t)) & 7u)) : 0u;
+      if (i < 4)
+        gsl_lo |= sl << (8 * i);
+      else
+        gsl_hi |= sl << (8 * (i - 4));
+      m &= m - 1u;
+    }
+  }
+  // Token slots in gather order (groups ascending, tokens ascending): group
+  // u owns positions [g_pre[u], g_pre[u] + T_u).
+  const int g_cnt = lane < U ? __builtin_popcount(g_mask & 0xFFu) : 0;
+  int g_pre = g_cnt;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(g_pre, d);
+    if (lane >= d) g_pre += t;
+  }
+  g_pre -= g_cnt;
+  auto grp_expert = [&](int uu) { return __builtin_amdgcn_readlane(g_exp, uu); };
+  auto grp_mask = [&](int uu) { return (uint32_t)__builtin_amdgcn_readlane((int)g_mask, uu); };
   if (g == 0) {
     for (int i = threadIdx.x; i < S; i += blockDim.x) {
       if (a.idx_out) a.idx_out[i] = s_idx[i];
@@ -546,65 +589,235 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // partials.
   constexpr int kHB = F::kUnitW + 4;
   float* sh = reinterpret_cast<float*>(s_buf);  // [S][UPS][kHB]
-  float* syp = sh + (size_t)S * UPS * kHB;       // [S][rows of this workgroup]
   const int RPWd = (D + GX - 1) / GX;            // output rows per workgroup
   const int RPV = (RPWd + kW - 1) / kW;          // rows per wave
   const int n0 = jx * RPWd;
+  // Matrix-core down projection (MXFP4 in MOE_LAYOUT_MFMA16, DNK > 0): the
+  // h slice goes to LDS as fp32 [S][FS], then as the B operand of the
+  // 16x16x128 scaled MFMA: four fp8 (E4M3) terms per value, h = 2^(e-127) *
+  // (c0 + c1 + c2 + c3), one E8M0 e per 32 values.  hb: [S][DNK][4 lane
+  // groups][4 terms][32 bytes]; hsc: [S][4 * DNK] exponents.
+  // Slot S of hb/hsc is all zeros: lanes without a token read it.
+  constexpr int kHbSlot = DNK * 512;
+  uint8_t* hb = s_buf + (((size_t)B * UG * kCh * 16 + 15) & ~(size_t)15);  // after the activations
+  uint8_t* hsc = hb + (size_t)(S + 1) * kHbSlot;
+  float* syp = DNK > 0 ? reinterpret_cast<float*>(hsc + (((size_t)(S + 1) * 4 * DNK + 15) & ~(size_t)15))
+                       : sh + (size_t)S * UPS * kHB;  // [S][rows of this workgroup]
   const int UD = RPV * UPS;                      // (row, slice-unit) pairs per wave per expert
   const int ub = lane % UPS;                     // this lane's unit inside the slice row
   // Where this lane's down unit lives: unit xcd*UPS + ub of row n, or, in
   // the tiled layout, unit (xcd*UPS + ub) % UPT of row c*D + n of the
   // [(Fd/256)*D][256] matrix, c = (xcd*UPS + ub) / UPT.
   constexpr int UPT = kTileCols / F::kUnitW;
+  const bool tiled = a.down.layout == MOE_LAYOUT_TILE256;
   const int du_row = xcd * UPS + ub;
-  const int dunit = a.down.tiled ? du_row % UPT : du_row;
-  const int64_t drow0 = a.down.tiled ? (int64_t)(du_row / UPT) * D : 0;
-  const int dK = a.down.tiled ? kTileCols : Fd;
+  const int dunit = tiled ? du_row % UPT : du_row;
+  const int64_t drow0 = tiled ? (int64_t)(du_row / UPT) * D : 0;
+  const int dK = tiled ? kTileCols : Fd;
   const uint32_t dsh = (uint32_t)dunit & 3u;
-  typename F::Raw dring[kRingDN][MAXU_DN];
-  auto load_dn = [&](int uu, typename F::Raw(&dst)[MAXU_DN]) {
+  // Matrix-core lane roles: A row / B and C column mi, lane group mg; the
+  // lane's A block for k-step ks is block xcd*UPS + 4ks + mg of row
+  // n0 + w*RPV + mi (an MFMA16 block number, so one load covers 1088
+  // contiguous bytes at the full shape).
+  const int mi = lane & 15, mg = lane >> 4;
+  const int drl = w * RPV + mi;
+  const bool drow_ok = mi < RPV && drl < RPWd && n0 + drl < D;
+  // Every lane's rows and blocks exist (the full layer shape): no masking.
+  const bool dn_full = RPV == 16 && RPWd % 16 == 0 && n0 + RPWd <= D && UPS % 4 == 0;
+  int dblk[DNK > 0 ? DNK : 1];
+  bool dok[DNK > 0 ? DNK : 1];
+#pragma unroll
+  for (int ks = 0; ks < DNK; ++ks) {
+    dok[ks] = drow_ok && 4 * ks + mg < UPS;
+    dblk[ks] = dok[ks] ? (int)mfma16_block(n0 + drl, xcd * UPS + 4 * ks + mg, D) : 0;
+  }
+  constexpr int kDnSlot = DNK > 0 ? DNK : MAXU_DN;
+  typename F::Raw dring[kRingDN][kDnSlot];
+  // Slots past the last expert load this XCD's first h words instead: the
+  // h gather has just read them, so the final waits of the ring are cache
+  // hits rather than trips to another XCD's weights.
+  const uint8_t* hot = reinterpret_cast<const uint8_t*>(ht + f0);
+  auto load_dn = [&](int uu, typename F::Raw(&dst)[kDnSlot]) {
     const bool live = uu < U;
-    const int ex = s_grp[live ? uu : U - 1].expert;
-    const uint16_t* ds = a.down.scale ? reinterpret_cast<const uint16_t*>(
-                                            reinterpret_cast<const uint8_t*>(a.down.scale) + ex * a.down.scale_stride)
-                                      : nullptr;
+    const int ex = grp_expert(live ? uu : U - 1);
+    if constexpr (DNK > 0) {
+      const typename F::Row all{live ? a.down.base + ex * a.down.stride : hot};
 #pragma unroll
-    for (int j = 0; j < MAXU_DN; ++j) {
-      const int v = lane + kWave * j;
-      const int rloc = w * RPV + v / UPS;
-      const bool ok = live && v < UD && rloc < RPWd && n0 + rloc < D;
-      const typename F::Row rw = F::row(a.down.base + ex * a.down.stride, ds, ok ? drow0 + n0 + rloc : 0, dK);
-      F::load(rw, ok ? dunit : 0, dst[j]);
-    }
-  };
-  auto compute_dn = [&](int uu, const typename F::Raw(&src)[MAXU_DN]) {
-    consume(src);
-    const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_grp[uu].mask);
-    for (uint32_t m = mask & 0xFFu; m != 0u; m &= m - 1u) {  // tokens ascending
-      const int t = __builtin_ctz(m);
-      const int s = t * k + (int)((mask >> (8 + 3 * t)) & 7u);
-      const float* hx = sh + (s * UPS + ub) * kHB;
-      // The lane's rows share one unit of h: read it from LDS once.
-      float hreg[kHB];
-      if (MAXU_DN > 1) {
-#pragma unroll
-        for (int c = 0; c < kHB / 4; ++c) {
-          const float4 v4 = *reinterpret_cast<const float4*>(hx + 4 * c);
-          hreg[4 * c] = v4.x;
-          hreg[4 * c + 1] = v4.y;
-          hreg[4 * c + 2] = v4.z;
-          hreg[4 * c + 3] = v4.w;
-        }
-      }
-      const float* hu = MAXU_DN > 1 ? hreg : hx;
+      for (int ks = 0; ks < DNK; ++ks) F::load(all, live ? dblk[ks] : 0, dst[ks]);
+    } else {
+      const uint16_t* ds = a.down.scale ? reinterpret_cast<const uint16_t*>(
+                                              reinterpret_cast<const uint8_t*>(a.down.scale) + ex * a.down.scale_stride)
+                                        : nullptr;
 #pragma unroll
       for (int j = 0; j < MAXU_DN; ++j) {
         const int v = lane + kWave * j;
         const int rloc = w * RPV + v / UPS;
-        const bool ok = v < UD && rloc < RPWd && n0 + rloc < D;
-        float pr = ok ? F::dn_dot(src[j], dsh, hu) : 0.0f;
-        pr = group_sum_dpp<UPS>(pr);
-        if (ok && ub == 0) syp[s * RPWd + rloc] = pr;
+        const bool ok = live && v < UD && rloc < RPWd && n0 + rloc < D;
+        const typename F::Row rw =
+            live ? F::row(a.down.base + ex * a.down.stride, ds, ok ? drow0 + n0 + rloc : 0, dK)
+                 : F::row(hot, reinterpret_cast<const uint16_t*>(hot), 0, dK);
+        F::load(rw, ok ? dunit : 0, dst[j]);
+      }
+    }
+  };
+  // Matrix-core path: once the workgroup's rows of h are out, its waves
+  // claim token slots (groups ascending, kGatherBatch at a time), read their
+  // h slices (the XCD's d_ff columns) and write them to LDS as the MFMA B
+  // operand: four fp8 (E4M3) terms per value under one E8M0 exponent per 32
+  // values.  With every group's down weights already in the prologue slots
+  // (U <= kRingDN - 1) the down projection is a plain loop over the groups.
+  constexpr int kGatherBatch = 3;
+  const bool dn_walk = U <= kRingDN - 1;
+  auto gather_batch = [&]() -> bool {  // false once every slot is claimed
+    int i0 = 0;
+    if (lane == 0) i0 = atomicAdd(&s_next, kGatherBatch);
+    i0 = __builtin_amdgcn_readfirstlane(i0);
+    if (i0 >= S) return false;
+    const int per_slot = DNK * 32;  // lanes of one slot: 4 values each, zeros past FS
+    const bool act = lane < per_slot;
+    const int fl = 4 * lane;
+    const bool inb = act && fl < FS;
+    int sl[kGatherBatch];
+#pragma unroll
+    for (int b = 0; b < kGatherBatch; ++b) {
+      const int i = min(i0 + b, S - 1);
+      const int u = (int)__builtin_popcountll(__ballot(lane < U && g_pre <= i)) - 1;
+      const int pos = i - __builtin_amdgcn_readlane(g_pre, u);
+      const uint32_t tab = (uint32_t)__builtin_amdgcn_readlane((int)(pos < 4 ? gsl_lo : gsl_hi), u);
+      sl[b] = (int)((tab >> (8 * (pos & 3))) & 0xFFu);
+    }
+    auto hp = [&](int q) { return ht + (int64_t)sl[q >> 2] * Fd + f0 + fl + (q & 3); };
+    uint64_t v[4 * kGatherBatch];
+    bool valid[4 * kGatherBatch];
+#pragma unroll
+    for (int q = 0; q < 4 * kGatherBatch; ++q) {
+      valid[q] = inb && i0 + (q >> 2) < S;
+      v[q] = valid[q] ? ld_xcd(hp(q)) : 0ull;
+    }
+    const int rr = await_tags<4 * kGatherBatch>(hp, v, valid, tag, wall_clock64(), &s_timeout);
+    trace_rereads += rr << 16;
+#pragma unroll
+    for (int b = 0; b < kGatherBatch; ++b) {
+      if (i0 + b >= S) break;
+      float x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = valid[4 * b + i] ? __uint_as_float(payload_of(v[4 * b + i])) : 0.0f;
+      // The 8 lanes of a 32-value block agree on its exponent e, which puts
+      // the block maximum in [128, 256): every term stays a normal or zero
+      // E4M3 value well inside its range.
+      float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+      mx = fmaxf(mx, dpp_f<0xB1>(mx));   // quad_perm [1,0,3,2]
+      mx = fmaxf(mx, dpp_f<0x4E>(mx));   // quad_perm [2,3,0,1]
+      mx = fmaxf(mx, dpp_f<0x141>(mx));  // row_half_mirror: the other quad of the 8
+      const int e = max((int)((__float_as_uint(mx) >> 23) & 0xFFu) - 7, 1);
+      const float scale = __uint_as_float((uint32_t)(254 - e) << 23);  // 2^(127 - e), exact
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] *= scale;
+      // hb byte q of lane group g, k-step ks holds value 128ks + 64(q/16) +
+      // 16g + ((q%16)^1): the E2M1 nibble order pairs weight 2j+1 with the
+      // lower K position, so values are stored pair-swapped.
+      const int r = fl & 127, ks = fl >> 7;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(hb + (size_t)sl[b] * kHbSlot +
+                                                  ((ks * 4 + ((r & 63) >> 4)) * 4) * 32 + (r >> 6) * 16 + (r & 15));
+#pragma unroll
+      for (int term = 0; term < 4; ++term) {
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(x[1], x[0], 0, false);
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(x[3], x[2], d, true);
+        if (act) dst[term * 8] = (uint32_t)d;
+        if (term < 3) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
+          x[1] -= lo.x;
+          x[0] -= lo.y;
+          x[3] -= hi.x;
+          x[2] -= hi.y;
+        }
+      }
+      if (act && (lane & 7) == 0) hsc[sl[b] * 4 * DNK + (fl >> 5)] = (uint8_t)e;
+    }
+    return true;
+  };
+  auto compute_dn = [&](int uu, const typename F::Raw(&src)[kDnSlot]) {
+    consume(src);
+    const uint32_t mask = grp_mask(uu);
+    if constexpr (DNK > 0) {
+      typedef int v8i __attribute__((ext_vector_type(8)));
+      typedef float v4f __attribute__((ext_vector_type(4)));
+      v8i A[DNK];
+      int ea[DNK];
+#pragma unroll
+      for (int ks = 0; ks < DNK; ++ks) {
+        uint32_t e, q[4];
+        F::unpack(src[ks], (uint32_t)dblk[ks] & 3u, e, q);
+        // Rows or blocks outside the matrix contribute zeros (E2M1 has no
+        // NaN, and a unit scale keeps the products finite).
+        A[ks] = v8i{(int)(dok[ks] ? q[0] : 0u), (int)(dok[ks] ? q[1] : 0u), (int)(dok[ks] ? q[2] : 0u),
+                    (int)(dok[ks] ? q[3] : 0u), 0, 0, 0, 0};
+        ea[ks] = dok[ks] ? (int)e : 127;
+      }
+      const int T = __builtin_popcount(mask & 0xFFu);
+      const uint32_t slo = (uint32_t)__builtin_amdgcn_readlane((int)gsl_lo, uu);
+      const uint32_t shi = (uint32_t)__builtin_amdgcn_readlane((int)gsl_hi, uu);
+      const int c = mi & 3;
+      for (int p0 = 0; p0 < T; p0 += 4) {  // four tokens (x four terms) per pass
+        const int tt = p0 + (mi >> 2);
+        const bool tok = tt < T;
+        const int sl = tok ? (int)(((tt < 4 ? slo : shi) >> (8 * (tt & 3))) & 0xFFu) : S;
+        v4f acc[DNK];
+#pragma unroll
+        for (int ks = 0; ks < DNK; ++ks) {
+          const uint4* bp = reinterpret_cast<const uint4*>(hb + (size_t)sl * kHbSlot + ((ks * 4 + mg) * 4 + c) * 32);
+          const uint4 b0 = bp[0], b1 = bp[1];
+          const int eb = hsc[sl * 4 * DNK + 4 * ks + mg];
+          const v8i Bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+          acc[ks] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[ks], Bv, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 0, 0,
+                                                                     ea[ks], 0, eb);
+        }
+#pragma unroll
+        for (int ks = 1; ks < DNK; ++ks) acc[0] += acc[ks];  // k-steps in order
+        // lane (tt, term c) holds rows 4mg..4mg+3 of column 4tt+c: sum the terms
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[0][r] = group_sum_dpp<4>(acc[0][r]);
+        if (tok && c == 0) {
+          if (dn_full) {  // the wave's 16 rows are all in range: one 16-byte store
+            *reinterpret_cast<float4*>(syp + sl * RPWd + w * 16 + 4 * mg) =
+                make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int rr = 4 * mg + r, rloc = w * RPV + rr;
+              if (rr < RPV && rloc < RPWd && n0 + rloc < D) syp[sl * RPWd + rloc] = acc[0][r];
+            }
+          }
+        }
+      }
+    } else {
+      for (uint32_t m = mask & 0xFFu; m != 0u; m &= m - 1u) {  // tokens ascending
+        const int t = __builtin_ctz(m);
+        const int s = t * k + (int)((mask >> (8 + 3 * t)) & 7u);
+        const float* hx = sh + (s * UPS + ub) * kHB;
+        // The lane's rows share one unit of h: read it from LDS once.
+        float hreg[kHB];
+        if (MAXU_DN > 1) {
+#pragma unroll
+          for (int c = 0; c < kHB / 4; ++c) {
+            const float4 v4 = *reinterpret_cast<const float4*>(hx + 4 * c);
+            hreg[4 * c] = v4.x;
+            hreg[4 * c + 1] = v4.y;
+            hreg[4 * c + 2] = v4.z;
+            hreg[4 * c + 3] = v4.w;
+          }
+        }
+        const float* hu = MAXU_DN > 1 ? hreg : hx;
+#pragma unroll
+        for (int j = 0; j < MAXU_DN; ++j) {
+          const int v = lane + kWave * j;
+          const int rloc = w * RPV + v / UPS;
+          const bool ok = v < UD && rloc < RPWd && n0 + rloc < D;
+          float pr = ok ? F::dn_dot(src[j], dsh, hu) : 0.0f;
+          pr = group_sum_dpp<UPS>(pr);
+          if (ok && ub == 0) syp[s * RPWd + rloc] = pr;
+        }
       }
     }
   };
@@ -621,7 +834,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       typename F::Raw ring[kRingGU][2][MAXU_GU];
       auto load_gu = [&](int uu, typename F::Raw(&dst)[2][MAXU_GU]) {
         const bool live = uu < U;
-        const int ex = s_grp[live ? uu : U - 1].expert;
+        const int ex = grp_expert(live ? uu : U - 1);
         const uint16_t* gs = a.gate.scale ? reinterpret_cast<const uint16_t*>(
                                                 reinterpret_cast<const uint8_t*>(a.gate.scale) + ex * a.gate.scale_stride)
                                           : nullptr;
@@ -640,7 +853,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       };
       auto compute_gu = [&](int uu, const typename F::Raw(&src)[2][MAXU_GU]) {
         consume(src);
-        const uint32_t mask = (uint32_t)__builtin_amdgcn_readfirstlane((int)s_grp[uu].mask);
+        const uint32_t mask = grp_mask(uu);
         for (uint32_t m = mask & 0xFFu; m != 0u; m &= m - 1u) {  // tokens ascending
           const int t = __builtin_ctz(m);
           float ag = 0.0f, au = 0.0f;
@@ -663,7 +876,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
           }
           ag = wave_sum_dpp(ag);
           au = wave_sum_dpp(au);
-          if (lane == 63) s_hv[w][t * k + (int)((mask >> (8 + 3 * t)) & 7u)] = silu(ag) * au;
+          // Publish h of this row at once: the down projection can start on
+          // an expert as soon as every row of it is out.
+          if (lane == 63)
+            st_dev(ht + (int64_t)(t * k + (int)((mask >> (8 + 3 * t)) & 7u)) * Fd + row,
+                   tagged(__float_as_uint(silu(ag) * au), tag));
         }
       };
 #pragma unroll
@@ -682,14 +899,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
             consume(ring[j]);
         }
       }
-      __builtin_amdgcn_wave_barrier();
-      // Publish this row of h for every slot (each slot belongs to one group).
-      for (int s = lane; s < S; s += kWave) st_dev(ht + (int64_t)s * Fd + row, tagged(__float_as_uint(s_hv[w][s]), tag));
     }
   }
   stamp(a, 6);
 
   // ---------------------------------------------------------------- 3. down (partials over the slice)
+  if constexpr (DNK == 0) {
   __syncthreads();  // the activation view of s_buf is no longer used
   stamp(a, 11);
   {
@@ -728,16 +943,32 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       __syncthreads();
     }
   }
+  }
+  if constexpr (DNK > 0) {
+    __syncthreads();  // every row of this workgroup is published
+    stamp(a, 11);
+    while (gather_batch()) {
+    }
+    stamp(a, 12);
+    if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints + 13] = (uint64_t)trace_rereads;
+    __syncthreads();
+  }
   stamp(a, 7);
-  for (int base = 0; base < U; base += kRingDN) {
+  if (DNK > 0 && dn_walk) {  // every group's down weights are in the prologue slots
 #pragma unroll
-    for (int j = 0; j < kRingDN; ++j) {
-      load_dn(base + j + kRingDN - 1, dring[(j + kRingDN - 1) % kRingDN]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (base + j < U)
-        compute_dn(base + j, dring[j]);
-      else
-        consume(dring[j]);
+    for (int j = 0; j < kRingDN - 1; ++j)
+      if (j < U) compute_dn(j, dring[j]);
+  } else {
+    for (int base = 0; base < U; base += kRingDN) {
+#pragma unroll
+      for (int j = 0; j < kRingDN; ++j) {
+        load_dn(base + j + kRingDN - 1, dring[(j + kRingDN - 1) % kRingDN]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (base + j < U)
+          compute_dn(base + j, dring[j]);
+        else
+          consume(dring[j]);
+      }
     }
   }
   __syncthreads();
@@ -797,34 +1028,51 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
 }
 
-template <class F, int MAXU_GU, int MAXU_DN, int UPS>
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK>
 hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS>), dim3(grid), dim3(kW * kWave), 0, s, a);
+  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK>), dim3(grid), dim3(kW * kWave), 0, s, a);
   return hipGetLastError();
 }
 
-template <class F, int UPS>
+// DNK: k-steps of the matrix-core down projection (0: vector path).
+template <class F, int UPS, int DNK>
 hipError_t launch_fused_f(const FusedArgs& a, int grid, int gu_units, int dn_units, hipStream_t s) {
-  if (gu_units > kWave) {
-    return dn_units > kWave ? launch_fused_t<F, 2, 2, UPS>(a, grid, s) : launch_fused_t<F, 2, 1, UPS>(a, grid, s);
+  if (DNK > 0) {
+    return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, DNK>(a, grid, s) : launch_fused_t<F, 1, 1, UPS, DNK>(a, grid, s);
   }
-  return dn_units > kWave ? launch_fused_t<F, 1, 2, UPS>(a, grid, s) : launch_fused_t<F, 1, 1, UPS>(a, grid, s);
+  if (gu_units > kWave) {
+    return dn_units > kWave ? launch_fused_t<F, 2, 2, UPS, 0>(a, grid, s) : launch_fused_t<F, 2, 1, UPS, 0>(a, grid, s);
+  }
+  return dn_units > kWave ? launch_fused_t<F, 1, 2, UPS, 0>(a, grid, s) : launch_fused_t<F, 1, 1, UPS, 0>(a, grid, s);
 }
 
 template <class F>
 hipError_t launch_fused_ups(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s) {
   switch (ups) {
-    case 1: return launch_fused_f<F, 1>(a, grid, gu_units, dn_units, s);
-    case 2: return launch_fused_f<F, 2>(a, grid, gu_units, dn_units, s);
-    case 4: return launch_fused_f<F, 4>(a, grid, gu_units, dn_units, s);
-    case 8: return launch_fused_f<F, 8>(a, grid, gu_units, dn_units, s);
-    case 16: return launch_fused_f<F, 16>(a, grid, gu_units, dn_units, s);
+    case 1: return launch_fused_f<F, 1, 0>(a, grid, gu_units, dn_units, s);
+    case 2: return launch_fused_f<F, 2, 0>(a, grid, gu_units, dn_units, s);
+    case 4: return launch_fused_f<F, 4, 0>(a, grid, gu_units, dn_units, s);
+    case 8: return launch_fused_f<F, 8, 0>(a, grid, gu_units, dn_units, s);
+    case 16: return launch_fused_f<F, 16, 0>(a, grid, gu_units, dn_units, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// MXFP4 with the down projections in MOE_LAYOUT_MFMA16 (d_ff slices of at
+// most 256 columns per XCD).
+inline hipError_t launch_fused_mfma(const FusedArgs& a, int grid, int gu_units, int ups, hipStream_t s) {
+  switch (ups) {
+    case 1: return launch_fused_f<MxFmt, 1, 1>(a, grid, gu_units, 0, s);
+    case 2: return launch_fused_f<MxFmt, 2, 1>(a, grid, gu_units, 0, s);
+    case 4: return launch_fused_f<MxFmt, 4, 1>(a, grid, gu_units, 0, s);
+    case 8: return launch_fused_f<MxFmt, 8, 2>(a, grid, gu_units, 0, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 // One instantiation set per weight format (each in its own translation unit).
 hipError_t launch_mx(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
+hipError_t launch_mx_mfma(const FusedArgs& a, int grid, int gu_units, int ups, hipStream_t s);
 hipError_t launch_q2k(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
 hipError_t launch_int4(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
 

@@ -9,5 +9,9 @@ hipError_t launch_mx(const FusedArgs& a, int grid, int gu_units, int dn_units, i
   return launch_fused_ups<MxFmt>(a, grid, gu_units, dn_units, ups, s);
 }
 
+hipError_t launch_mx_mfma(const FusedArgs& a, int grid, int gu_units, int ups, hipStream_t s) {
+  return launch_fused_mfma(a, grid, gu_units, ups, s);
+}
+
 }  // namespace fused
 }  // namespace moe

@@ -7,6 +7,8 @@
 // covers 64 consecutive units of a row: fully used cache lines.  The R rows'
 // raw units are loaded first, then reused for every token; the per-lane
 // partial dots are summed across the wave at the end.
+#include <type_traits>
+
 #include "units.h"
 
 namespace moe {
@@ -49,6 +51,30 @@ __device__ __forceinline__ void rows_dot_tiled(const uint8_t* base, const uint16
     for (int r = 0; r < R; ++r) F::load(F::row(base, sc, (int64_t)c * N + n[r], kTileCols), uu, raw[r]);
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] += F::dot(raw[r], (uint32_t)uu & 3u, x + (int64_t)F::kUnitW * u);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+}
+
+// Same for MXFP4 rows stored in MOE_LAYOUT_MFMA16 (block j of row n is
+// block mfma16_block(n, j, N) of the matrix).
+template <int R>
+__device__ __forceinline__ void rows_dot_mfma16(const uint8_t* base, const int (&n)[R], int N, int K,
+                                                const float* __restrict__ x, float (&acc)[R]) {
+  const int U = K / 32;
+  const MxFmt::Row all{base};
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int u = lane_id(); u < U; u += kWave) {
+    MxFmt::Raw raw[R];
+    int b[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      b[r] = (int)mfma16_block(n[r], u, N);
+      MxFmt::load(all, b[r], raw[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] += MxFmt::dot(raw[r], (uint32_t)b[r] & 3u, x + (int64_t)32 * u);
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
@@ -152,10 +178,19 @@ __global__ __launch_bounds__(256) void down_kernel(WeightRef down, int D, int Fd
   for (int t = 0; t < grp.n; ++t) {
     const int64_t ts = (int64_t)grp.tok[t] * k + grp.slot[t];
     float acc[kDownR];
-    if (down.tiled)
-      rows_dot_tiled<F, kDownR>(dbase, ds, rn, D, Fd, h + ts * Fd, acc);
-    else
-      rows_dot<F, kDownR>(rows, Fd, h + ts * Fd, acc);
+    bool done = false;
+    if constexpr (std::is_same<F, MxFmt>::value) {
+      if (down.layout == MOE_LAYOUT_MFMA16) {
+        rows_dot_mfma16<kDownR>(dbase, rn, D, Fd, h + ts * Fd, acc);
+        done = true;
+      }
+    }
+    if (!done) {
+      if (down.layout == MOE_LAYOUT_TILE256)
+        rows_dot_tiled<F, kDownR>(dbase, ds, rn, D, Fd, h + ts * Fd, acc);
+      else
+        rows_dot<F, kDownR>(rows, Fd, h + ts * Fd, acc);
+    }
     if (lane_id() == 0) {
 #pragma unroll
       for (int r = 0; r < kDownR; ++r)

@@ -184,8 +184,15 @@ struct WeightRef {
   const uint16_t* scale;    // INT4 scales (else null)
   int64_t stride;           // bytes between experts
   int64_t scale_stride;     // bytes between experts' scales
-  int tiled;                // 1: MOE_LAYOUT_TILE256 (row c*N + n of a [(K/256)*N][256] matrix), 0: row-major
+  int layout;               // enum moe_layout (gate and up are always MOE_LAYOUT_ROWS)
 };
+
+// Block number of block j (32 columns) of row n of an MXFP4 matrix [N][K] in
+// MOE_LAYOUT_MFMA16: tile c = j/8, half j/4 % 2, quarter j % 4, 16-row group
+// n/16, row n % 16.
+__device__ __forceinline__ int64_t mfma16_block(int64_t n, int j, int N) {
+  return ((((int64_t)(j >> 3) * (N >> 4) + (n >> 4)) * 2 + ((j >> 2) & 1)) * 4 + (j & 3)) * 16 + (n & 15);
+}
 
 // Columns per tile of MOE_LAYOUT_TILE256.
 constexpr int kTileCols = 256;
@@ -219,14 +226,17 @@ hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
 // n < N, i < tile (elements of 2 or 4 bytes).
 hipError_t launch_tile_rows(const void* src, void* dst, int64_t N, int tiles, int tile_elems, int elem_bytes,
                             hipStream_t s);
+// MXFP4 [N][K/32][17] -> MOE_LAYOUT_MFMA16 (N % 16 == 0, K % 256 == 0).
+hipError_t launch_tile_mfma16(const uint8_t* src, uint8_t* dst, int N, int K, hipStream_t s);
 
 // Single-launch layer (routing, gate/up, down and combine in one kernel).
 struct FusedShape {
   bool ok;
+  bool mfma;  // matrix-core down projection (MXFP4, MOE_LAYOUT_MFMA16)
   int gu_units, dn_units, ups;
 };
 int fused_grid_size();
-FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx);
+FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx, int down_layout);
 // XCD count of the current device, measured once per device (the probe
 // synchronises `s`; scratch needs grid uint32).  xcd_count(): 0 not measured
 // yet, -1 placement unsuitable for the single-launch layer, else the count.

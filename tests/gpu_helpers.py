@@ -108,11 +108,14 @@ class Layer:
                 self.q[0][1], self.q[1][1], self.q[2][1], self.q[0][2], self.q[1][2], self.q[2][2],
                 self.q[0][3], self.q[1][3], self.q[2][3], down_layout=down_layout)
         else:
-            if down_layout == "tile256":
+            if down_layout in ("tile256", "mfma16"):
                 buf, stride = self.bytes[synth.PROJ_DOWN]
                 bt = torch.empty_like(buf)
                 for e in range(E):
-                    moe.moe_tile_weights(fmt, buf.data_ptr() + e * stride, D, F, bt.data_ptr() + e * stride)
+                    if down_layout == "tile256":
+                        moe.moe_tile_weights(fmt, buf.data_ptr() + e * stride, D, F, bt.data_ptr() + e * stride)
+                    else:
+                        moe.moe_tile_weights_mfma16(buf.data_ptr() + e * stride, D, F, bt.data_ptr() + e * stride)
                 self.bytes[synth.PROJ_DOWN] = (bt, stride)
                 torch.cuda.synchronize()
             self.desc = moe.make_layer_desc(

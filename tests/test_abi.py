@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == moe.ABI_VERSION == 3
     for st in range(7):
         assert moe.moe_status_string(st)
     assert moe.moe_status_string(0) == "ok"
@@ -121,6 +121,16 @@ def test_layout_validation_on_host(L):
     assert T(2, FAKE, None, 8, 256, FAKE, None, None) == 1           # INT4 without scales
     assert T(0, FAKE, FAKE, 8, 256, FAKE, FAKE, None) == 1           # scales only for INT4
     assert T(2, FAKE + 4, FAKE, 8, 256, FAKE, FAKE, None) == 6       # INT4 codes 16-byte aligned
+    d.d_ff = 2048
+    d.down_layout = 2                                   # MFMA16: MXFP4 only
+    d.format = 1
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, ws_ok, None, None, None) == 1
+    d.format, d.d_ff = 0, 2080                          # and d_ff % 256 == 0
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, ws_ok, None, None, None) == 2
+    M = L.moe_tile_weights_mfma16
+    assert M(None, 16, 256, FAKE, None) == 1                          # null source
+    assert M(FAKE, 16, 224, FAKE, None) == 2                          # K % 256
+    assert M(FAKE, 24, 256, FAKE, None) == 2                          # N % 16
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

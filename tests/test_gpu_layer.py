@@ -2,8 +2,9 @@
 the fp64 oracle, in all three formats, at small shapes and at the full layer
 shape (256 experts, d_model 4096, d_ff 2048, top-6) for B = 1 and B = 8.
 
-Both down-projection layouts (row-major as published, and 256-column tiles)
-are covered; the full-shape Q2_K and INT4 runs use the tiled layout.
+The down-projection layouts (row-major as published, 256-column tiles, and
+for MXFP4 the tiles ordered for the matrix cores) are covered; the
+full-shape Q2_K and INT4 runs use the tiled layout.
 
 Invariants: run-to-run bitwise determinism, identical tokens give identical
 rows (and 6 unique experts), and a token's result does not depend on the
@@ -38,8 +39,11 @@ def _parity(L, xb, what):
     return assert_parity(y, yo, what=what), y
 
 
-@pytest.mark.parametrize("layout", ["rows", "tile256"])
-@pytest.mark.parametrize("fmt", ["mxfp4", "q2k", "int4g32"])
+FMT_LAYOUTS = [(f, l) for f in ("mxfp4", "q2k", "int4g32") for l in ("rows", "tile256")] + [("mxfp4", "mfma16")]
+MX_LAYOUTS = ["rows", "tile256", "mfma16"]
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS)
 @pytest.mark.parametrize("B", [1, 3, 8])
 def test_layer_small(fmt, B, layout):
     L = layer(fmt, 32, 512, 256, 6, seed=11, down_layout=layout)
@@ -47,7 +51,7 @@ def test_layer_small(fmt, B, layout):
     _parity(L, xb, f"{fmt} small B={B} {layout}")
 
 
-@pytest.mark.parametrize("layout", ["rows", "tile256"])
+@pytest.mark.parametrize("layout", MX_LAYOUTS)
 def test_layer_small_several_tiles(layout):
     # d_ff 1024: four 256-column tiles per down row (two per XCD slice on an
     # 8-XCD chip would need d_ff 4096; here slices are smaller than a tile)
@@ -56,7 +60,7 @@ def test_layer_small_several_tiles(layout):
         _parity(L, synth.token_bf16(550 + B, B, 256), f"d_ff 1024 B={B} {layout}")
 
 
-@pytest.mark.parametrize("layout", ["rows", "tile256"])
+@pytest.mark.parametrize("layout", MX_LAYOUTS)
 def test_layer_multi_launch_fallback_shape(layout):
     # d_model 8192 has more MXFP4 blocks per row than the single-launch
     # kernel keeps per lane, so the layer runs as separate launches.
@@ -72,7 +76,7 @@ def test_layer_small_ragged_topk_and_experts():
         _parity(L, synth.token_bf16(600 + B, B, 96), f"ragged B={B}")
 
 
-@pytest.mark.parametrize("layout", ["rows", "tile256"])
+@pytest.mark.parametrize("layout", MX_LAYOUTS)
 @pytest.mark.parametrize("B", [1, 8])
 def test_layer_full_mxfp4(B, layout):
     L = layer("mxfp4", 256, 4096, 2048, down_layout=layout)
@@ -95,7 +99,7 @@ def _single_launch(L, B):
     return moe.moe_layer_decode_traced(L.desc, x, y, L.workspace(B)) is not None
 
 
-@pytest.mark.parametrize("layout", ["rows", "tile256"])
+@pytest.mark.parametrize("layout", MX_LAYOUTS)
 def test_layer_invariants_full_shape(layout):
     L = layer("mxfp4", 256, 4096, 2048, down_layout=layout)
     assert _single_launch(L, 1) and _single_launch(L, 8), "full layer shape should run as one launch"

@@ -1,5 +1,6 @@
-"""GPU block permutation to the 256-column tiled layout (moe_tile_weights):
-bit-exact against the same permutation written with numpy reshapes.
+"""GPU block permutations to the 256-column tiled layout (moe_tile_weights)
+and to its matrix-core refinement (moe_tile_weights_mfma16): bit-exact
+against the same permutations written with numpy reshapes.
 
 Inputs are the seeded generators' blocks (MXFP4, Q2_K) and seeded random INT4
 words and scales; the expected bytes never come from the HIP path."""
@@ -43,3 +44,20 @@ def test_tile_int4_codes_and_scales_bit_exact(n, k):
     torch.cuda.synchronize()
     assert np.array_equal(host(qt), _tiled(q.reshape(-1), n, k // 256))
     assert np.array_equal(host(st, np.uint16), _tiled(s.reshape(-1), n, k // 256))
+
+
+def _mfma16(blocks: np.ndarray, n: int, k: int) -> np.ndarray:
+    """[n][k/32] blocks -> [tile c][row group n/16][half][quarter][row n%16] (MOE_LAYOUT_MFMA16)."""
+    b = blocks.reshape(n // 16, 16, k // 256, 2, 4, 17)          # (R, i, c, h, q, byte)
+    return np.ascontiguousarray(b.transpose(2, 0, 3, 4, 1, 5)).reshape(-1)
+
+
+@pytest.mark.parametrize("n,k", [(16, 256), (48, 768), (4096, 2048)])
+def test_tile_mfma16_bit_exact(n, k):
+    key = synth.tensor_key(190 + n, synth.TAG_MXFP4, 0, 0, 2)
+    blocks = synth.mxfp4_blocks(key, n * k // 32)
+    src = dev(blocks.reshape(-1))
+    dst = torch.empty_like(src)
+    moe.moe_tile_weights_mfma16(src, n, k, dst)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dst), _mfma16(blocks.reshape(-1), n, k))
