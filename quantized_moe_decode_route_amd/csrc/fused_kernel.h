@@ -32,6 +32,8 @@
 // the workspace and the kernel runs to completion.
 #pragma once
 
+#include <type_traits>
+
 #include "units.h"
 
 namespace moe {
@@ -288,6 +290,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   __shared__ uint32_t s_mask[MOE_MAX_EXPERTS];  // per expert: tokens that picked it and at which rank
   __shared__ double s_part[kW][kMaxTok];
   __shared__ int s_next;                 // matrix-core path: next token slot to gather
+  __shared__ int s_gu_next;              // next gate/up work item
   __shared__ int s_U;
   __shared__ int s_timeout;
   __shared__ int s_jx;
@@ -307,7 +310,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
                                          __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   for (int i = threadIdx.x; i < MOE_MAX_EXPERTS; i += blockDim.x) s_mask[i] = 0u;
-  if (threadIdx.x == 0) s_next = 0;
+  if (threadIdx.x == 0) {
+    s_next = 0;
+    s_gu_next = 0;
+  }
 
   // Activations for gate/up: requested now, staged in LDS ([t][chunk][unit],
   // so lanes read consecutive chunks) after the router logits.  B * units <=
@@ -555,16 +561,6 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       m &= m - 1u;
     }
   }
-  // Token slots in gather order (groups ascending, tokens ascending): group
-  // u owns positions [g_pre[u], g_pre[u] + T_u).
-  const int g_cnt = lane < U ? __builtin_popcount(g_mask & 0xFFu) : 0;
-  int g_pre = g_cnt;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int t = __shfl_up(g_pre, d);
-    if (lane >= d) g_pre += t;
-  }
-  g_pre -= g_cnt;
   auto grp_expert = [&](int uu) { return __builtin_amdgcn_readlane(g_exp, uu); };
   auto grp_mask = [&](int uu) { return (uint32_t)__builtin_amdgcn_readlane((int)g_mask, uu); };
   if (g == 0) {
@@ -661,7 +657,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
   };
   // Matrix-core path: once the workgroup's rows of h are out, its waves
-  // claim token slots (groups ascending, kGatherBatch at a time), read their
+  // claim token slots (kGatherBatch at a time), read their
   // h slices (the XCD's d_ff columns) and write them to LDS as the MFMA B
   // operand: four fp8 (E4M3) terms per value under one E8M0 exponent per 32
   // values.  With every group's down weights already in the prologue slots
@@ -677,15 +673,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     const bool act = lane < per_slot;
     const int fl = 4 * lane;
     const bool inb = act && fl < FS;
-    int sl[kGatherBatch];
+    int sl[kGatherBatch];  // every slot t*k + r of the call is some group's
 #pragma unroll
-    for (int b = 0; b < kGatherBatch; ++b) {
-      const int i = min(i0 + b, S - 1);
-      const int u = (int)__builtin_popcountll(__ballot(lane < U && g_pre <= i)) - 1;
-      const int pos = i - __builtin_amdgcn_readlane(g_pre, u);
-      const uint32_t tab = (uint32_t)__builtin_amdgcn_readlane((int)(pos < 4 ? gsl_lo : gsl_hi), u);
-      sl[b] = (int)((tab >> (8 * (pos & 3))) & 0xFFu);
-    }
+    for (int b = 0; b < kGatherBatch; ++b) sl[b] = min(i0 + b, S - 1);
     auto hp = [&](int q) { return ht + (int64_t)sl[q >> 2] * Fd + f0 + fl + (q & 3); };
     uint64_t v[4 * kGatherBatch];
     bool valid[4 * kGatherBatch];
@@ -821,85 +811,111 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       }
     }
   };
-#pragma unroll
-  for (int j = 0; j < kRingDN - 1; ++j) {
-    load_dn(j, dring[j]);
-    __builtin_amdgcn_sched_barrier(0);  // slots are requested in ring order
-  }
+  // Gate/up work items are (expert group, row) pairs of this workgroup's
+  // rows, groups ascending, handed out by an LDS counter: a wave takes its
+  // next item when it requests the item's weights (kRingGU - 1 items ahead),
+  // so waves that get their data sooner take more items and all finish
+  // together.  A wave's first pass also requests the down prologue between
+  // its first gate/up slots, so the gate/up data that the ring waits for
+  // first is not queued behind down weights used only after the exchange.
+  static_assert(2 * Rings<F>::kGU >= Rings<F>::kDN - 1, "down prologue fits the first gate/up pass");
   {
-    for (int r = w; r < RPW; r += kW) {
-      const int rl = jx * RPW + r;  // row inside the slice
-      if (rl >= FS) break;
-      const int row = f0 + rl;
-      typename F::Raw ring[kRingGU][2][MAXU_GU];
-      auto load_gu = [&](int uu, typename F::Raw(&dst)[2][MAXU_GU]) {
-        const bool live = uu < U;
-        const int ex = grp_expert(live ? uu : U - 1);
-        const uint16_t* gs = a.gate.scale ? reinterpret_cast<const uint16_t*>(
-                                                reinterpret_cast<const uint8_t*>(a.gate.scale) + ex * a.gate.scale_stride)
-                                          : nullptr;
-        const uint16_t* us = a.up.scale ? reinterpret_cast<const uint16_t*>(
-                                              reinterpret_cast<const uint8_t*>(a.up.scale) + ex * a.up.scale_stride)
+    const int NR = max(0, min(RPW, FS - jx * RPW));  // rows of this workgroup
+    const int NI = NR * U;
+    const float inv_nr = 1.0f / (float)max(NR, 1);
+    auto group_of = [&](int it) {  // it / NR for 0 <= it < NI (exact after the correction)
+      int q = (int)((float)it * inv_nr);
+      q -= q * NR > it ? 1 : 0;
+      q += (q + 1) * NR <= it ? 1 : 0;
+      return q;
+    };
+    auto take = [&]() {
+      int i = 0;
+      if (lane == 0) i = atomicAdd(&s_gu_next, 1);
+      return __builtin_amdgcn_readfirstlane(i);
+    };
+    typename F::Raw ring[kRingGU][2][MAXU_GU];
+    int item[kRingGU];  // item in each slot (>= NI: a dead slot)
+    auto load_gu = [&](int it, typename F::Raw(&dst)[2][MAXU_GU]) {
+      const bool live = it < NI;
+      const int uu = live ? group_of(it) : U - 1;
+      const int row = f0 + jx * RPW + (live ? it - uu * NR : 0);
+      const int ex = grp_expert(uu);
+      const uint16_t* gs = a.gate.scale ? reinterpret_cast<const uint16_t*>(
+                                              reinterpret_cast<const uint8_t*>(a.gate.scale) + ex * a.gate.scale_stride)
                                         : nullptr;
-        const typename F::Row rg = F::row(a.gate.base + ex * a.gate.stride, gs, row, D);
-        const typename F::Row ru = F::row(a.up.base + ex * a.up.stride, us, row, D);
+      const uint16_t* us = a.up.scale ? reinterpret_cast<const uint16_t*>(
+                                            reinterpret_cast<const uint8_t*>(a.up.scale) + ex * a.up.scale_stride)
+                                      : nullptr;
+      const typename F::Row rg = F::row(a.gate.base + ex * a.gate.stride, gs, row, D);
+      const typename F::Row ru = F::row(a.up.base + ex * a.up.stride, us, row, D);
+#pragma unroll
+      for (int j = 0; j < MAXU_GU; ++j) {
+        const int u = lane + kWave * j;
+        const int ul = (live && u < UG) ? u : 0;
+        F::load(rg, ul, dst[0][j]);
+        F::load(ru, ul, dst[1][j]);
+      }
+    };
+    auto compute_gu = [&](int it, const typename F::Raw(&src)[2][MAXU_GU]) {
+      consume(src);
+      const int uu = group_of(it);
+      const int row = f0 + jx * RPW + (it - uu * NR);
+      const uint32_t mask = grp_mask(uu);
+      for (uint32_t m = mask & 0xFFu; m != 0u; m &= m - 1u) {  // tokens ascending
+        const int t = __builtin_ctz(m);
+        float ag = 0.0f, au = 0.0f;
 #pragma unroll
         for (int j = 0; j < MAXU_GU; ++j) {
           const int u = lane + kWave * j;
-          const int ul = (live && u < UG) ? u : 0;
-          F::load(rg, ul, dst[0][j]);
-          F::load(ru, ul, dst[1][j]);
-        }
-      };
-      auto compute_gu = [&](int uu, const typename F::Raw(&src)[2][MAXU_GU]) {
-        consume(src);
-        const uint32_t mask = grp_mask(uu);
-        for (uint32_t m = mask & 0xFFu; m != 0u; m &= m - 1u) {  // tokens ascending
-          const int t = __builtin_ctz(m);
-          float ag = 0.0f, au = 0.0f;
+          if (u < UG) {
+            uint32_t xs[F::kXDw];
 #pragma unroll
-          for (int j = 0; j < MAXU_GU; ++j) {
-            const int u = lane + kWave * j;
-            if (u < UG) {
-              uint32_t xs[F::kXDw];
-#pragma unroll
-              for (int c = 0; c < kCh; ++c) {
-                const uint4 p = xl[(t * kCh + c) * UG + u];
-                xs[4 * c] = p.x;
-                xs[4 * c + 1] = p.y;
-                xs[4 * c + 2] = p.z;
-                xs[4 * c + 3] = p.w;
-              }
-              ag += F::gu_dot(src[0][j], (uint32_t)u & 3u, xs);
-              au += F::gu_dot(src[1][j], (uint32_t)u & 3u, xs);
+            for (int c = 0; c < kCh; ++c) {
+              const uint4 p = xl[(t * kCh + c) * UG + u];
+              xs[4 * c] = p.x;
+              xs[4 * c + 1] = p.y;
+              xs[4 * c + 2] = p.z;
+              xs[4 * c + 3] = p.w;
             }
+            ag += F::gu_dot(src[0][j], (uint32_t)u & 3u, xs);
+            au += F::gu_dot(src[1][j], (uint32_t)u & 3u, xs);
           }
-          ag = wave_sum_dpp(ag);
-          au = wave_sum_dpp(au);
-          // Publish h of this row at once: the down projection can start on
-          // an expert as soon as every row of it is out.
-          if (lane == 63)
-            st_dev(ht + (int64_t)(t * k + (int)((mask >> (8 + 3 * t)) & 7u)) * Fd + row,
-                   tagged(__float_as_uint(silu(ag) * au), tag));
         }
-      };
-#pragma unroll
-      for (int j = 0; j < kRingGU - 1; ++j) {
-        load_gu(j, ring[j]);
-        __builtin_amdgcn_sched_barrier(0);  // slots are requested in ring order
+        ag = wave_sum_dpp(ag);
+        au = wave_sum_dpp(au);
+        // Publish h of this row at once.
+        if (lane == 63)
+          st_dev(ht + (int64_t)(t * k + (int)((mask >> (8 + 3 * t)) & 7u)) * Fd + row,
+                 tagged(__float_as_uint(silu(ag) * au), tag));
       }
-      for (int base = 0; base < U; base += kRingGU) {
+    };
 #pragma unroll
-        for (int j = 0; j < kRingGU; ++j) {
-          load_gu(base + j + kRingGU - 1, ring[(j + kRingGU - 1) % kRingGU]);
-          __builtin_amdgcn_sched_barrier(0);
-          if (base + j < U)
-            compute_gu(base + j, ring[j]);
-          else
-            consume(ring[j]);
-        }
-      }
+    for (int j = 0; j < kRingGU - 1; ++j) {
+      item[j] = take();
+      load_gu(item[j], ring[j]);
+      __builtin_amdgcn_sched_barrier(0);  // slots are requested in ring order
     }
+    auto pass = [&](auto first) {
+#pragma unroll
+      for (int j = 0; j < kRingGU; ++j) {
+        item[(j + kRingGU - 1) % kRingGU] = take();
+        load_gu(item[(j + kRingGU - 1) % kRingGU], ring[(j + kRingGU - 1) % kRingGU]);
+        if constexpr (decltype(first)::value) {
+          if (2 * j < kRingDN - 1) load_dn(2 * j, dring[2 * j]);
+          if (2 * j + 1 < kRingDN - 1) load_dn(2 * j + 1, dring[2 * j + 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (item[j] < NI)
+          compute_gu(item[j], ring[j]);
+        else
+          consume(ring[j]);
+      }
+    };
+    pass(std::true_type{});
+    // items are taken in increasing order: once a pass ends on a dead slot,
+    // every later slot is dead too
+    while (item[kRingGU - 1] < NI) pass(std::false_type{});
   }
   stamp(a, 6);
 
