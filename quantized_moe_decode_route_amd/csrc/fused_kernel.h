@@ -811,6 +811,62 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       }
     }
   };
+  // Matrix-core down for prologue slots j0 .. j0 + kDnBatch - 1 in one
+  // straight-line block (requires dn_full and groups of at most 4 tokens).
+  // Slots past the last group compute on the zero operand and store nothing.
+  constexpr int kDnBatch = (Rings<F>::kDN - 1 + 1) / 2;
+  auto down_walk_batch = [&](auto j0c) {
+    if constexpr (DNK > 0) {
+      constexpr int j0 = decltype(j0c)::value;
+      typedef int v8i __attribute__((ext_vector_type(8)));
+      typedef float v4f __attribute__((ext_vector_type(4)));
+      const int c = mi & 3, tt = mi >> 2;
+      v8i A[kDnBatch][DNK], Bv[kDnBatch][DNK];
+      int ea[kDnBatch][DNK], eb[kDnBatch][DNK], sl[kDnBatch];
+      bool st[kDnBatch];
+#pragma unroll
+      for (int b = 0; b < kDnBatch; ++b) {
+        const int j = j0 + b;
+        if (j >= kRingDN - 1) continue;
+        consume(dring[j]);
+        const bool live = j < U;
+        const uint32_t mask = grp_mask(live ? j : U - 1);
+        const int T = live ? __builtin_popcount(mask & 0xFFu) : 0;
+        const bool tok = tt < T;
+        const uint32_t tab = (uint32_t)__builtin_amdgcn_readlane((int)gsl_lo, live ? j : U - 1);
+        sl[b] = tok ? (int)((tab >> (8 * (tt & 3))) & 0xFFu) : S;
+        st[b] = tok && c == 0;
+#pragma unroll
+        for (int ks = 0; ks < DNK; ++ks) {
+          uint32_t e, q[4];
+          F::unpack(dring[j][ks], (uint32_t)dblk[ks] & 3u, e, q);
+          A[b][ks] = v8i{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
+          ea[b][ks] = (int)e;
+          const uint4* bp = reinterpret_cast<const uint4*>(hb + (size_t)sl[b] * kHbSlot + ((ks * 4 + mg) * 4 + c) * 32);
+          const uint4 b0 = bp[0], b1 = bp[1];
+          Bv[b][ks] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+          eb[b][ks] = hsc[sl[b] * 4 * DNK + 4 * ks + mg];
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < kDnBatch; ++b) {
+        const int j = j0 + b;
+        if (j >= kRingDN - 1) continue;
+        v4f acc[DNK];
+#pragma unroll
+        for (int ks = 0; ks < DNK; ++ks)
+          acc[ks] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[b][ks], Bv[b][ks], v4f{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                     4, 0, 0, ea[b][ks], 0, eb[b][ks]);
+#pragma unroll
+        for (int ks = 1; ks < DNK; ++ks) acc[0] += acc[ks];  // k-steps in order
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[0][r] = group_sum_dpp<4>(acc[0][r]);
+        if (st[b])
+          *reinterpret_cast<float4*>(syp + sl[b] * RPWd + w * 16 + 4 * mg) =
+              make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+      }
+    }
+  };
   // Gate/up work items are (expert group, row) pairs of this workgroup's
   // rows, groups ascending, handed out by an LDS counter: a wave takes its
   // next item when it requests the item's weights (kRingGU - 1 items ahead),
@@ -970,7 +1026,13 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     __syncthreads();
   }
   stamp(a, 7);
-  if (DNK > 0 && dn_walk) {  // every group's down weights are in the prologue slots
+  if (DNK > 0 && dn_walk && B <= 4 && dn_full) {
+    // Every group's down weights are in the prologue slots and every group
+    // has at most 4 tokens (one MFMA pass): the groups are computed in
+    // straight-line batches, so their LDS reads and MFMAs overlap.
+    down_walk_batch(std::integral_constant<int, 0>{});
+    down_walk_batch(std::integral_constant<int, kDnBatch>{});
+  } else if (DNK > 0 && dn_walk) {  // every group's down weights are in the prologue slots
 #pragma unroll
     for (int j = 0; j < kRingDN - 1; ++j)
       if (j < U) compute_dn(j, dring[j]);
