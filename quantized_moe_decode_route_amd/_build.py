@@ -23,10 +23,17 @@ HIP_FLAGS = [
 ]
 
 
+# The single-launch layer's few atomics are issued by one lane and their
+# results used much later; the atomic optimizer would rewrite them into a
+# lane-0 atomic plus readfirstlane, which waits for the result on the spot.
+FUSED_FLAGS = ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+
+
 def _compile(src: str) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *HIP_FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    extra = FUSED_FLAGS if os.path.basename(src).startswith("fused") else []
+    cmd = [HIPCC, *HIP_FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -279,9 +279,14 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   const int lane = lane_id();
   const int B = a.B, k = a.k, E = a.E, D = a.D, Fd = a.Fd;
   const int S = B * k;  // (token, rank) slots
-  stamp(a, 0);
+  const uint64_t t_start = wall_clock64();  // trace slot 0, stored with slot 1 (no store this early)
   uint32_t* ctr = reinterpret_cast<uint32_t*>(a.ws + a.L.counters);
-  uint32_t tag = ctr[kCtrEpoch] + 1u;  // this call's epoch
+  // This call's epoch, read with a scalar load: a vector load here would
+  // make the first use of the tag wait for the x and atomic requests issued
+  // after it.  (Workgroup 0 advances the counter only after every workgroup
+  // has read it.)
+  typedef const __attribute__((address_space(4))) uint32_t ConstU32;
+  uint32_t tag = ((ConstU32*)ctr)[kCtrEpoch] + 1u;
   if (tag == 0u) tag = 1u;              // tags start at 1 (the workspace starts zeroed)
 
   __shared__ int32_t s_idx[kMaxSlots];
@@ -304,28 +309,24 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // behind them.
   uint32_t xcd_arrival = 0;
   int trace_rereads = 0;  // thread 0: re-read passes of the logit (low half) and h (high half) waits
-  if (threadIdx.x == 0) {
-    s_timeout = 0;
-    xcd_arrival = __hip_atomic_fetch_add(ctr + kCtrXcdBase + xcd, 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_WORKGROUP);
-  }
+  if (threadIdx.x == 0) s_timeout = 0;
+  // Requested right after this thread's first router loads (its result is
+  // needed only after the logits), so nothing waits for it before them.
+  bool arrival_pending = true;
+  auto take_arrival = [&]() {
+    if (arrival_pending && threadIdx.x == 0)
+      xcd_arrival = __hip_atomic_fetch_add(ctr + kCtrXcdBase + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    arrival_pending = false;
+  };
   for (int i = threadIdx.x; i < MOE_MAX_EXPERTS; i += blockDim.x) s_mask[i] = 0u;
   if (threadIdx.x == 0) {
     s_next = 0;
     s_gu_next = 0;
   }
 
-  // Activations for gate/up: requested now, staged in LDS ([t][chunk][unit],
-  // so lanes read consecutive chunks) after the router logits.  B * units <=
-  // 2 * blockDim for every shape this kernel accepts.
   const int UG = F::units(D);
   uint32_t xraw[2][F::kXRaw];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int i = threadIdx.x + q * kW * kWave;
-    if (i < B * UG) F::load_x(a.x + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);
-  }
-  __syncthreads();
+  // (The LDS words cleared above are next used after the logits' barriers.)
 
   // ---------------------------------------------------------------- 1. routing
   uint64_t* lg = reinterpret_cast<uint64_t*>(a.ws + a.L.logit_tags);  // [B][E][2]: high, low halves
@@ -334,12 +335,13 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     double acc[kMaxTok];
 #pragma unroll
     for (int t = 0; t < kMaxTok; ++t) acc[t] = 0.0;
-    for (int c = 8 * threadIdx.x; c < D; c += 8 * kW * kWave) {
+    auto chunk = [&](const int c) {
       const float4 w0 = *reinterpret_cast<const float4*>(row + c);
       const float4 w1 = *reinterpret_cast<const float4*>(row + c + 4);
       uint4 xall[kMaxTok];  // every token's activations requested before the first use
 #pragma unroll
       for (int t = 0; t < kMaxTok; ++t) xall[t] = *reinterpret_cast<const uint4*>(a.x + (int64_t)min(t, B - 1) * D + c);
+      take_arrival();
 #pragma unroll
       for (int t = 0; t < kMaxTok; ++t) {
         if (t < B) {
@@ -354,6 +356,13 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
           acc[t] = __builtin_fma((double)w1.w, (double)bf16_to_f32(xv.w >> 16), acc[t]);
         }
       }
+    };
+    // One 8-weight chunk per thread in straight-line code when the row
+    // fits (d_model <= 4096): no loop header for the compiler to wait at.
+    if (D <= 8 * kW * kWave) {
+      if (8 * (int)threadIdx.x < D) chunk(8 * threadIdx.x);
+    } else {
+      for (int c = 8 * threadIdx.x; c < D; c += 8 * kW * kWave) chunk(c);
     }
 #pragma unroll
     for (int t = 0; t < kMaxTok; ++t) {
@@ -376,26 +385,17 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
     __syncthreads();
   }
+  take_arrival();  // workgroups without a router row
+  if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints] = t_start;
   stamp(a, 1);
-  uint4* xl = reinterpret_cast<uint4*>(s_buf);
+  // Activations for gate/up: requested now that the router weights are in,
+  // staged in LDS ([t][chunk][unit], so lanes read consecutive chunks) after
+  // the routing, which hides their latency.  B * units <= 2 * blockDim for
+  // every shape this kernel accepts.
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int i = threadIdx.x + q * kW * kWave;
-    if (i < B * UG) {
-      const int t = i / UG, u = i - (i / UG) * UG;
-      uint32_t xs[F::kXDw];
-      F::pack_x(xraw[q], xs);
-#pragma unroll
-      for (int c = 0; c < kCh; ++c)
-        xl[(t * kCh + c) * UG + u] = make_uint4(xs[4 * c], xs[4 * c + 1], xs[4 * c + 2], xs[4 * c + 3]);
-    }
-  }
-  if (threadIdx.x == 0) {
-    s_jx = (int)(xcd_arrival % (uint32_t)GX);
-    if (a.trace) {
-      a.trace[blockIdx.x * kTracePoints + kTracePoints - 2] = (uint64_t)xcd;
-      a.trace[blockIdx.x * kTracePoints + kTracePoints - 1] = (uint64_t)xcd_arrival;
-    }
+    if (i < B * UG) F::load_x(a.x + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);
   }
   stamp(a, 2);
 
@@ -529,6 +529,33 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
     if (lane == 0) s_U = base;
   }
+  if (threadIdx.x == 0) {  // the arrival counter has long returned by now
+    s_jx = (int)(xcd_arrival % (uint32_t)GX);
+    if (a.trace) {
+      a.trace[blockIdx.x * kTracePoints + kTracePoints - 2] = (uint64_t)xcd;
+      a.trace[blockIdx.x * kTracePoints + kTracePoints - 1] = (uint64_t)xcd_arrival;
+    }
+  }
+  // Stage the activations.  They are opaque until here, so the compiler
+  // cannot hoist their rearrangement into the routing, where it would wait
+  // for x.
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int i = 0; i < F::kXRaw; ++i) asm volatile("" : "+v"(xraw[q][i]));
+  uint4* xl = reinterpret_cast<uint4*>(s_buf);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = threadIdx.x + q * kW * kWave;
+    if (i < B * UG) {
+      const int t = i / UG, u = i - (i / UG) * UG;
+      uint32_t xs[F::kXDw];
+      F::pack_x(xraw[q], xs);
+#pragma unroll
+      for (int c = 0; c < kCh; ++c)
+        xl[(t * kCh + c) * UG + u] = make_uint4(xs[4 * c], xs[4 * c + 1], xs[4 * c + 2], xs[4 * c + 3]);
+    }
+  }
   if constexpr (DNK > 0) {  // the zero B operand (slot S) read by lanes without a token
     uint8_t* hb0 = s_buf + (((size_t)B * UG * kCh * 16 + 15) & ~(size_t)15);
     for (int i = threadIdx.x; i < DNK * 512 / 16; i += kW * kWave)
@@ -544,11 +571,13 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // gsl_hi).
   static_assert(kMaxSlots <= kWave, "one group per lane");
   int g_exp;
-  uint32_t g_mask, gsl_lo = 0u, gsl_hi = 0u;
+  uint32_t g_mask, gsl_lo = 0u, gsl_hi = 0u;  // slot tables: filled after gate/up
   {
     const LayerGroup gr = s_grp[min(lane, U - 1)];
     g_exp = gr.expert;
     g_mask = gr.mask;
+  }
+  auto fill_slot_tables = [&]() {
     uint32_t m = g_mask & 0xFFu;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -560,7 +589,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         gsl_hi |= sl << (8 * (i - 4));
       m &= m - 1u;
     }
-  }
+  };
   auto grp_expert = [&](int uu) { return __builtin_amdgcn_readlane(g_exp, uu); };
   auto grp_mask = [&](int uu) { return (uint32_t)__builtin_amdgcn_readlane((int)g_mask, uu); };
   if (g == 0) {
@@ -974,6 +1003,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     while (item[kRingGU - 1] < NI) pass(std::false_type{});
   }
   stamp(a, 6);
+  fill_slot_tables();
 
   // ---------------------------------------------------------------- 3. down (partials over the slice)
   if constexpr (DNK == 0) {
