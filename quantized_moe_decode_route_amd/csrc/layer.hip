@@ -36,38 +36,46 @@ __global__ __launch_bounds__(256) void combine_kernel(int D, int B, int k, const
   *reinterpret_cast<float4*>(y + (int64_t)t * D + n) = acc;
 }
 
-// fp64 -> bfloat16 bits, round to nearest even, without double rounding:
-// first to fp32 with round-to-odd (24 >= 8 + 2 bits), then fp32 -> bf16 RNE.
-__device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
-  float f = (float)v;
-  const double back = (double)f;
-  if (back != v && !__builtin_isnan(v)) {
-    uint32_t u = __float_as_uint(f);
-    if (__builtin_fabs(back) > __builtin_fabs(v)) u -= 1u;  // step toward zero
-    u |= 1u;
-    f = __uint_as_float(u);
-  }
-  return f32_to_bf16_rne(f);
-}
-
-// One workgroup per token: x = bf16_rne(h / sqrt(mean(h^2) + eps)) in fp64.
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h, int D, double eps,
-                                                      uint16_t* __restrict__ out) {
+// One workgroup per token: x = bf16_rne(h / sqrt(mean(h^2) + eps)) in fp64,
+// the sum of squares in the chunk order of rms_total.  Rows of at most 4096
+// elements (a multiple of 8, 16-byte aligned) take one chunk per thread with
+// both of its loads issued at once; other rows walk their chunks in the same
+// order element by element.
+__global__ __launch_bounds__(kRmsThreads) void rmsnorm_kernel(const float* __restrict__ h, int D, double eps,
+                                                              uint16_t* __restrict__ out) {
   const int t = blockIdx.x;
   const float* row = h + (int64_t)t * D;
+  uint16_t* xo = out + (int64_t)t * D;
+  const int i = threadIdx.x;
+  __shared__ double s_part[kRmsWaves];
+  const bool vec = D % 8 == 0 && D <= 8 * kRmsThreads && (((uintptr_t)h | (uintptr_t)out) & 15u) == 0;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
   double ss = 0.0;
-  for (int i = threadIdx.x; i < D; i += blockDim.x) {
-    const double v = row[i];
-    ss = __builtin_fma(v, v, ss);
+  if (vec) {
+    if (8 * i < D) {
+      a = *reinterpret_cast<const float4*>(row + 8 * i);
+      b = *reinterpret_cast<const float4*>(row + 8 * i + 4);
+      ss = rms_squares8(a, b, 0.0);
+    }
+  } else {
+    for (int c = i; 8 * c < D; c += kRmsThreads)
+      for (int j = 8 * c; j < min(8 * c + 8, D); ++j) {
+        const double v = row[j];
+        ss = __builtin_fma(v, v, ss);
+      }
   }
   ss = wave_sum_f64(ss);
-  __shared__ double s_part[4];
-  if (lane_id() == 0) s_part[threadIdx.x / kWave] = ss;
+  if (lane_id() == 0) s_part[i / kWave] = ss;
   __syncthreads();
-  const double tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
-  const double denom = sqrt(tot / D + eps);
-  for (int i = threadIdx.x; i < D; i += blockDim.x)
-    out[(int64_t)t * D + i] = (uint16_t)f64_to_bf16_rne((double)row[i] / denom);
+  const RmsScale sc = rms_scale(rms_total(s_part), D, eps);
+  if (vec) {
+    if (8 * i < D) *reinterpret_cast<uint4*>(xo + 8 * i) = rms_x8(a, b, sc);
+  } else {
+    // element by element (same values as rms_x8: the fast form only ever
+    // returns the correctly rounded quotient)
+    for (int c = i; 8 * c < D; c += kRmsThreads)
+      for (int j = 8 * c; j < min(8 * c + 8, D); ++j) xo[j] = (uint16_t)f64_to_bf16_rne((double)row[j] / sc.denom);
+  }
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int n) {
@@ -86,7 +94,7 @@ hipError_t launch_combine(int D, int B, int k, const uint8_t* ws, const WsLayout
 }
 
 hipError_t launch_rmsnorm_bf16(const float* h, int B, int D, double eps, uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(B), dim3(256), 0, s, h, D, eps, out);
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(B), dim3(kRmsThreads), 0, s, h, D, eps, out);
   return hipGetLastError();
 }
 

@@ -114,6 +114,88 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// fp64 -> bfloat16 bits, round to nearest even, without double rounding:
+// first to fp32 with round-to-odd (24 >= 8 + 2 bits), then fp32 -> bf16 RNE.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
+  float f = (float)v;
+  const double back = (double)f;
+  if (back != v && !__builtin_isnan(v)) {
+    uint32_t u = __float_as_uint(f);
+    if (__builtin_fabs(back) > __builtin_fabs(v)) u -= 1u;  // step toward zero
+    u |= 1u;
+    f = __uint_as_float(u);
+  }
+  return f32_to_bf16_rne(f);
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// x_i = bf16_rne(h_i / sqrt(mean(h^2) + eps)), fp64, for one row h[0..D).
+// The sum of squares has one fixed order, shared by the stand-alone norm
+// kernel and the single-launch layer (so their activations agree bit for
+// bit): the row is cut into 8-element chunks, thread i of 512 takes chunks
+// i, i+512, ... and adds their squares with fma in element order, each wave
+// sums its 64 lanes with the shfl-xor tree of wave_sum_f64, and the eight
+// wave sums are added as ((w0+w1)+(w2+w3))+((w4+w5)+(w6+w7)).
+constexpr int kRmsThreads = 512;
+constexpr int kRmsWaves = kRmsThreads / kWave;
+static_assert(kRmsWaves == 8, "the wave-sum order below names eight waves");
+
+__device__ __forceinline__ double rms_squares8(const float4& a, const float4& b, double ss) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ss = __builtin_fma((double)v[j], (double)v[j], ss);
+  return ss;
+}
+__device__ __forceinline__ double rms_total(const double* w) {
+  return ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+}
+
+// The divisor of one row.  `fast` allows the quotient to be formed as
+// h * r in fp32 (r = 1/denom rounded to fp32): it needs a finite, positive
+// denominator whose reciprocal is a normal fp32 number, which also bounds
+// every |h_i / denom| by sqrt(D) (eps >= 0).
+struct RmsScale {
+  double denom;
+  float r;
+  bool fast;
+};
+__device__ __forceinline__ RmsScale rms_scale(double total, int D, double eps) {
+  RmsScale s;
+  s.denom = sqrt(total / D + eps);
+  const double r = 1.0 / s.denom;
+  s.r = (float)r;
+  s.fast = s.denom > 0.0 && r > 0x1p-125 && r < 0x1p125;  // false for NaN and inf
+  return s;
+}
+
+// bf16_rne(h_j / denom) of eight elements, packed low element first.  Fast
+// form: q = RN32(h * r) lies within 1.5 fp32 ulps of the exact quotient
+// (one rounding in r, one in the product; in the subnormal range within one
+// ulp), so unless q's low 16 bits sit within 2 of the bf16 rounding midpoint
+// 0x8000, q and the exact quotient round to the same bfloat16, which is then
+// q's upper half after adding 0x8000 (no tie is possible).  Near a midpoint,
+// or without a fast scale, the exact fp64 quotient is rounded instead.
+__device__ __forceinline__ uint4 rms_x8(const float4& a, const float4& b, const RmsScale& s) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t o[4];
+  bool near = !s.fast;
+  if (s.fast) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t q0 = __float_as_uint(v[2 * j] * s.r), q1 = __float_as_uint(v[2 * j + 1] * s.r);
+      near |= ((q0 + 2u - 0x8000u) & 0xFFFFu) <= 4u;
+      near |= ((q1 + 2u - 0x8000u) & 0xFFFFu) <= 4u;
+      o[j] = __builtin_amdgcn_perm(q1 + 0x8000u, q0 + 0x8000u, 0x07060302u);
+    }
+  }
+  if (near) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      o[j] = f64_to_bf16_rne((double)v[2 * j] / s.denom) | (f64_to_bf16_rne((double)v[2 * j + 1] / s.denom) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // ---------------------------------------------------------------- workspace
 
 // One unique expert of a layer call and the (token, rank) pairs routed to it,

@@ -24,6 +24,61 @@ def test_rmsnorm_bit_exact():
         assert np.array_equal(host(x, np.uint16), oracle.rmsnorm_bf16(h.astype(np.float64), 1e-6))
 
 
+def _midpoint_rows(rng, B, D):
+    """Rows of 3 * (a bfloat16 value or a bfloat16 rounding midpoint in
+    [0.5, 1)), random signs: every h^2 has at most 22 significant bits, so
+    mean(h^2) is exact in any summation order and eps = 9 - mean makes the
+    divisor exactly 3: each quotient is then exactly a bfloat16 value or a
+    midpoint (a tie, rounded to even).  The odd rows move every element one
+    fp32 step (up or toward zero), which puts the quotients a fraction of an
+    fp32 step beside the midpoints."""
+    b = rng.integers(0x3F00, 0x3F80, size=(B, D)).astype(np.uint32)
+    half = np.where(rng.random((B, D)) < 0.75, 0x8000, 0).astype(np.uint32)
+    m = ((b << 16) | half).view(np.float32).astype(np.float64)
+    sign = np.where(rng.random((B, D)) < 0.5, -1.0, 1.0)
+    h = (3.0 * m * sign).astype(np.float32)
+    up = rng.random((B, D)) < 0.5
+    moved = np.where(up, np.nextafter(h, np.float32(np.inf)), np.nextafter(h, np.float32(0)))
+    h[1::2] = moved[1::2]
+    return h
+
+
+@pytest.mark.parametrize("D", [4096, 8192])
+def test_rmsnorm_midpoints_and_subnormals(D):
+    """The fast fp32 quotient must fall back to the exact fp64 one wherever it
+    could round differently: exact midpoints (ties to even), neighbours of
+    midpoints, quotients in the fp32 subnormal range and divisors whose
+    reciprocal is not a normal fp32 number.  D = 4096 takes the one-chunk-
+    per-thread path, D = 8192 the element walk."""
+    rng = np.random.default_rng(5)
+    h = _midpoint_rows(rng, 4, D)
+    for t in range(4):
+        mean = float(np.sum(h[t].astype(np.float64) ** 2) / D)
+        eps = max(9.0 - mean, 0.0)
+        if t % 2 == 0:
+            assert mean + eps == 9.0
+        x = torch.empty((1, D), dtype=torch.int16, device="cuda")
+        moe.moe_rmsnorm_bf16(dev(h[t:t + 1]), x, float(eps))
+        torch.cuda.synchronize()
+        want = oracle.rmsnorm_bf16(h[t:t + 1].astype(np.float64), float(eps))
+        assert np.array_equal(host(x, np.uint16), want), f"row {t}"
+    # subnormal quotients beside one large element; all-subnormal rows (1/denom
+    # beyond fp32); a zero row with eps > 0
+    tiny = (rng.standard_normal((3, D)) * 1e-42).astype(np.float32)
+    tiny[0, 17] = 1e3
+    tiny[2] = 0.0
+    x = torch.empty((3, D), dtype=torch.int16, device="cuda")
+    moe.moe_rmsnorm_bf16(dev(tiny), x, 1e-6)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(x, np.uint16)[:2], oracle.rmsnorm_bf16(tiny[:2].astype(np.float64), 1e-6)[:2])
+    got0 = host(x, np.uint16)[2]
+    assert np.all(got0 == 0)
+    x1 = torch.empty((1, D), dtype=torch.int16, device="cuda")
+    moe.moe_rmsnorm_bf16(dev(tiny[1:2]), x1, 0.0)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(x1, np.uint16), oracle.rmsnorm_bf16(tiny[1:2].astype(np.float64), 0.0))
+
+
 @pytest.mark.parametrize("B", [1, 8])
 def test_stack_teacher_forced(B):
     E, D, F, n_layers = 32, 512, 256, 4
