@@ -202,8 +202,12 @@ int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int
  * with h_0 = h_in (fp32 [B][D]); the result goes to h_out (fp32 [B][D],
  * may alias h_in).  Attention is outside this path.  The norm is an
  * unweighted RMSNorm: the pages keep norms in F32 ("The recipe") without
- * defining them.  eps: 1e-6 in the stacked-layer workload.
- * ws: >= moe_stack_workspace_bytes(B, D, F, E, top_k). */
+ * defining them.  eps: 1e-6 in the stacked-layer workload.  The sum of
+ * squares is taken in one fixed order (8-element chunks over 512 threads,
+ * fp64), so x_l is the same whether the norm runs as its own kernel or, for
+ * one token with MXFP4 MOE_LAYOUT_MFMA16 layers, inside the layer kernel.
+ * ws: >= moe_stack_workspace_bytes(B, D, F, E, top_k): one layer's
+ * workspace, x_l (bf16) and one fp32 residual state. */
 size_t moe_stack_workspace_bytes(int B, int D, int F, int E, int top_k);
 int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* h_in, int B,
                      float* h_out, double eps, void* ws, size_t ws_bytes, void* stream);

@@ -83,8 +83,12 @@ WeightRef wref(const void* base, int64_t stride, const uint16_t* scale, int64_t 
   return w;
 }
 
+// With hn set, the layer's activations are x = RMSNorm(hn) (bf16, eps): the
+// single-launch kernel forms them itself when it can (hn must not alias y),
+// otherwise the norm kernel writes them to xbuf first.
 int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, const float* residual, void* ws,
-               int32_t* idx_out, float* gw_out, void* const* events, hipStream_t s, uint64_t* trace = nullptr) {
+               int32_t* idx_out, float* gw_out, void* const* events, hipStream_t s, uint64_t* trace = nullptr,
+               const float* hn = nullptr, double eps = 0.0, uint16_t* xbuf = nullptr) {
   const int D = L->d_model, F = L->d_ff, E = L->n_experts, k = L->top_k;
   const WsLayout W = layer_ws_layout(B, D, F, E, k);
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -100,9 +104,19 @@ int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
   const int grid = fused_grid_size();
   int nx = xcd_count();
   if (nx == 0) nx = probe_xcd_count(reinterpret_cast<uint32_t*>(w + W.topo), grid, s);
-  if (nx > 0 && fused_shape(L->format, B, k, D, F, grid, nx, L->down_layout).ok) {
-    e = launch_fused_layer(L->format, L->router_w, x_bf16, g, u, d, E, D, F, k, B, w, W, y, residual, idx_out,
-                           gw_out, trace, s);
+  const FusedShape sh = nx > 0 ? fused_shape(L->format, B, k, D, F, grid, nx, L->down_layout) : FusedShape{};
+  const bool fused = nx > 0 && sh.ok;
+  // In-kernel norm for one token only: at B = 8 its redundant per-workgroup
+  // work (every workgroup normalises the whole batch) costs more than the
+  // separate norm kernel.
+  if (hn && !(fused && sh.mfma && B == 1 && D <= kFusedNormMaxD && D % 8 == 0 && hn != y)) {
+    if ((e = launch_rmsnorm_bf16(hn, B, D, eps, xbuf, s)) != hipSuccess) return hip_status(e);
+    x_bf16 = xbuf;
+    hn = nullptr;
+  }
+  if (fused) {
+    e = launch_fused_layer(L->format, L->router_w, x_bf16, hn, eps, g, u, d, E, D, F, k, B, w, W, y, residual,
+                           idx_out, gw_out, trace, s);
     if (e != hipSuccess) return hip_status(e);
   } else {
     if ((e = launch_route(L->router_w, E, D, x_bf16, B, k, w, W, idx_out, gw_out, nullptr, s)) != hipSuccess)
@@ -253,8 +267,9 @@ int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int
 size_t moe_stack_workspace_bytes(int B, int D, int F, int E, int top_k) {
   const size_t layer = moe_layer_workspace_bytes(B, D, F, E, top_k);
   if (!layer) return 0;
-  // + normalised activation (bf16) of the current layer
-  return layer + align256((size_t)B * D * sizeof(uint16_t));
+  // + normalised activation (bf16) of the current layer, + one fp32 residual
+  // state (layers alternate between it and h_out)
+  return layer + align256((size_t)B * D * sizeof(uint16_t)) + align256((size_t)B * D * sizeof(float));
 }
 
 int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* h_in, int B, float* h_out, double eps,
@@ -277,13 +292,18 @@ int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* h_
   if ((st = arch_check()) != MOE_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   uint16_t* xb = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + layer_bytes);
+  float* tmp = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + layer_bytes +
+                                        align256((size_t)B * D * sizeof(uint16_t)));
+  // Layer l reads h_l and writes h_{l+1} to another buffer (h_out for the
+  // last layer, the two alternating backwards from it), so a layer that
+  // normalises its own input never overwrites it.  If h_in aliases h_out
+  // and layer 0 would write h_out, layer 0 takes the separate norm kernel.
   const float* cur = h_in;
   for (int l = 0; l < n_layers; ++l) {
-    hipError_t e = launch_rmsnorm_bf16(cur, B, D, eps, xb, s);
-    if (e != hipSuccess) return hip_status(e);
-    st = layer_impl(&layers[l], xb, B, h_out, cur, ws, nullptr, nullptr, nullptr, s);
+    float* dst = (n_layers - 1 - l) % 2 == 0 ? h_out : tmp;
+    st = layer_impl(&layers[l], nullptr, B, dst, cur, ws, nullptr, nullptr, nullptr, s, nullptr, cur, eps, xb);
     if (st != MOE_OK) return st;
-    cur = h_out;
+    cur = dst;
   }
   return MOE_OK;
 }

@@ -105,13 +105,17 @@ int probe_xcd_count(uint32_t* scratch, int grid, hipStream_t s) {
   return nx = n;
 }
 
-hipError_t launch_fused_layer(int fmt, const float* router_w, const uint16_t* x, const WeightRef& gate,
-                              const WeightRef& up, const WeightRef& down, int E, int D, int Fd, int k, int B,
-                              uint8_t* ws, const WsLayout& L, float* y, const float* residual, int32_t* idx_out,
-                              float* gw_out, uint64_t* trace, hipStream_t s) {
+hipError_t launch_fused_layer(int fmt, const float* router_w, const uint16_t* x, const float* hn, double eps,
+                              const WeightRef& gate, const WeightRef& up, const WeightRef& down, int E, int D, int Fd,
+                              int k, int B, uint8_t* ws, const WsLayout& L, float* y, const float* residual,
+                              int32_t* idx_out, float* gw_out, uint64_t* trace, hipStream_t s) {
+  static_assert(kW == kRmsWaves, "the in-kernel norm sums over the norm kernel's eight waves");
+  if (hn && (B != 1 || D > kFusedNormMaxD || D % 8 || hn == y)) return hipErrorInvalidValue;
   FusedArgs a;
   a.router_w = router_w;
   a.x = x;
+  a.hn = hn;
+  a.eps = eps;
   a.gate = gate;
   a.up = up;
   a.down = down;
@@ -131,7 +135,11 @@ hipError_t launch_fused_layer(int fmt, const float* router_w, const uint16_t* x,
   const int grid = fused_grid_size();
   const FusedShape sh = fused_shape(fmt, B, k, D, Fd, grid, a.nx, down.layout);
   if (!sh.ok) return hipErrorInvalidValue;
-  if (sh.mfma) return fused::launch_mx_mfma(a, grid, sh.gu_units, sh.ups, s);
+  if (sh.mfma) {
+    return hn ? fused::launch_mx_mfma_norm(a, grid, sh.gu_units, sh.ups, s)
+              : fused::launch_mx_mfma(a, grid, sh.gu_units, sh.ups, s);
+  }
+  if (hn) return hipErrorInvalidValue;  // the in-kernel norm is built for the matrix-core path only
   switch (fmt) {
     case MOE_FMT_MXFP4: return fused::launch_mx(a, grid, sh.gu_units, sh.dn_units, sh.ups, s);
     case MOE_FMT_Q2K: return fused::launch_q2k(a, grid, sh.gu_units, sh.dn_units, sh.ups, s);

@@ -75,10 +75,6 @@ __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
                                                                false));
 }
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ int dpp_i(int v, int old) {
-  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
-}
 
 // Sum over the wave in a fixed tree; the total lands in lane 63.
 __device__ __forceinline__ float wave_sum_dpp(float v) {
@@ -102,22 +98,6 @@ __device__ __forceinline__ float group_sum_dpp(float v) {
   return v;
 }
 
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ double dpp_d(double v) {
-  const int lo = dpp_i<CTRL, ROW_MASK>(__double2loint(v), 0);
-  const int hi = dpp_i<CTRL, ROW_MASK>(__double2hiint(v), 0);
-  return __hiloint2double(hi, lo);
-}
-
-__device__ __forceinline__ double wave_sum_dpp_f64(double v) {
-  v += dpp_d<0xB1>(v);
-  v += dpp_d<0x4E>(v);
-  v += dpp_d<0x141>(v);
-  v += dpp_d<0x140>(v);
-  v += dpp_d<0x142, 0xA>(v);
-  v += dpp_d<0x143, 0xC>(v);
-  return v;
-}
 
 // (value, index) with "better" = larger value, then lower index.
 __device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
@@ -187,7 +167,11 @@ struct LayerGroup {
 
 struct FusedArgs {
   const float* router_w;
-  const uint16_t* x;  // bf16 bits [B][D]
+  const uint16_t* x;  // bf16 bits [B][D]; unused when hn is set
+  // When set: the residual stream h [1][D] (fp32), normalised in the kernel
+  // into x = bf16_rne(h / sqrt(mean(h^2) + eps)) (B = 1, d_model <= 4096).
+  const float* hn;
+  double eps;
   WeightRef gate, up, down;
   uint8_t* ws;
   WsLayout L;
@@ -268,7 +252,7 @@ struct Rings<Int4Fmt> {  // its gate/up unpacking keeps more registers live
 };
 constexpr int kSpinBatch = 12;  // tagged words a thread reads before its first wait
 
-template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK>
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM>
 __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a) {
   constexpr int kCh = F::kXDw / 4;  // 16-byte chunks of one unit's staged activations
   constexpr int kRingGU = Rings<F>::kGU;
@@ -280,6 +264,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   const int B = a.B, k = a.k, E = a.E, D = a.D, Fd = a.Fd;
   const int S = B * k;  // (token, rank) slots
   const uint64_t t_start = wall_clock64();  // trace slot 0, stored with slot 1 (no store this early)
+  // The pointers of the first loads, fetched with the first group of scalar
+  // loads (otherwise the compiler may fetch them after the LDS set-up).
+  asm volatile("" ::"s"(a.router_w), "s"(NORM ? (const void*)a.hn : (const void*)a.x));
   uint32_t* ctr = reinterpret_cast<uint32_t*>(a.ws + a.L.counters);
   // This call's epoch, read with a scalar load: a vector load here would
   // make the first use of the tag wait for the x and atomic requests issued
@@ -294,6 +281,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   __shared__ LayerGroup s_grp[kMaxSlots];
   __shared__ uint32_t s_mask[MOE_MAX_EXPERTS];  // per expert: tokens that picked it and at which rank
   __shared__ double s_part[kW][kMaxTok];
+  __shared__ double s_rms[kW];  // in-kernel norm: the waves' sums of squares
   __shared__ int s_next;                 // matrix-core path: next token slot to gather
   __shared__ int s_gu_next;              // next gate/up work item
   __shared__ int s_U;
@@ -330,40 +318,25 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 
   // ---------------------------------------------------------------- 1. routing
   uint64_t* lg = reinterpret_cast<uint64_t*>(a.ws + a.L.logit_tags);  // [B][E][2]: high, low halves
-  for (int e = g; e < E; e += G) {
-    const float* row = a.router_w + (int64_t)e * D;
-    double acc[kMaxTok];
+  // Router logit partial sums over one 8-element chunk of every token.
+  auto dot8 = [&](double (&acc)[kMaxTok], const float4& w0, const float4& w1, const uint4 (&xall)[kMaxTok]) {
 #pragma unroll
-    for (int t = 0; t < kMaxTok; ++t) acc[t] = 0.0;
-    auto chunk = [&](const int c) {
-      const float4 w0 = *reinterpret_cast<const float4*>(row + c);
-      const float4 w1 = *reinterpret_cast<const float4*>(row + c + 4);
-      uint4 xall[kMaxTok];  // every token's activations requested before the first use
-#pragma unroll
-      for (int t = 0; t < kMaxTok; ++t) xall[t] = *reinterpret_cast<const uint4*>(a.x + (int64_t)min(t, B - 1) * D + c);
-      take_arrival();
-#pragma unroll
-      for (int t = 0; t < kMaxTok; ++t) {
-        if (t < B) {
-          const uint4 xv = xall[t];
-          acc[t] = __builtin_fma((double)w0.x, (double)bf16_to_f32(xv.x & 0xFFFFu), acc[t]);
-          acc[t] = __builtin_fma((double)w0.y, (double)bf16_to_f32(xv.x >> 16), acc[t]);
-          acc[t] = __builtin_fma((double)w0.z, (double)bf16_to_f32(xv.y & 0xFFFFu), acc[t]);
-          acc[t] = __builtin_fma((double)w0.w, (double)bf16_to_f32(xv.y >> 16), acc[t]);
-          acc[t] = __builtin_fma((double)w1.x, (double)bf16_to_f32(xv.z & 0xFFFFu), acc[t]);
-          acc[t] = __builtin_fma((double)w1.y, (double)bf16_to_f32(xv.z >> 16), acc[t]);
-          acc[t] = __builtin_fma((double)w1.z, (double)bf16_to_f32(xv.w & 0xFFFFu), acc[t]);
-          acc[t] = __builtin_fma((double)w1.w, (double)bf16_to_f32(xv.w >> 16), acc[t]);
-        }
+    for (int t = 0; t < kMaxTok; ++t) {
+      if (t < B) {
+        const uint4 xv = xall[t];
+        acc[t] = __builtin_fma((double)w0.x, (double)bf16_to_f32(xv.x & 0xFFFFu), acc[t]);
+        acc[t] = __builtin_fma((double)w0.y, (double)bf16_to_f32(xv.x >> 16), acc[t]);
+        acc[t] = __builtin_fma((double)w0.z, (double)bf16_to_f32(xv.y & 0xFFFFu), acc[t]);
+        acc[t] = __builtin_fma((double)w0.w, (double)bf16_to_f32(xv.y >> 16), acc[t]);
+        acc[t] = __builtin_fma((double)w1.x, (double)bf16_to_f32(xv.z & 0xFFFFu), acc[t]);
+        acc[t] = __builtin_fma((double)w1.y, (double)bf16_to_f32(xv.z >> 16), acc[t]);
+        acc[t] = __builtin_fma((double)w1.z, (double)bf16_to_f32(xv.w & 0xFFFFu), acc[t]);
+        acc[t] = __builtin_fma((double)w1.w, (double)bf16_to_f32(xv.w >> 16), acc[t]);
       }
-    };
-    // One 8-weight chunk per thread in straight-line code when the row
-    // fits (d_model <= 4096): no loop header for the compiler to wait at.
-    if (D <= 8 * kW * kWave) {
-      if (8 * (int)threadIdx.x < D) chunk(8 * threadIdx.x);
-    } else {
-      for (int c = 8 * threadIdx.x; c < D; c += 8 * kW * kWave) chunk(c);
     }
+  };
+  // Reduces one router row's partial sums and publishes its logits.
+  auto publish_logits = [&](int e, double (&acc)[kMaxTok]) {
 #pragma unroll
     for (int t = 0; t < kMaxTok; ++t) {
       if (t < B) {
@@ -384,6 +357,73 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       st_dev(p + 1, tagged((uint32_t)__double2loint(s), tag));
     }
     __syncthreads();
+  };
+  if constexpr (NORM) {
+    // One token (B = 1): its activations are the RMS-normalised residual
+    // stream, computed here in the chunk order of rms_total (thread i:
+    // elements 8i..8i+7, d_model <= 4096) while the first router row is on
+    // its way.  Each thread keeps its chunk for the logits and leaves it in
+    // LDS (s_buf as x [D], until the activations are staged) for gate/up.
+    // The loads are issued unconditionally (clamped to valid rows), h first:
+    // the norm then waits for h alone while the router row is in flight.
+    const bool mine = 8 * (int)threadIdx.x < D;
+    const int c8 = mine ? 8 * (int)threadIdx.x : 0;
+    float4 ha = *reinterpret_cast<const float4*>(a.hn + c8);
+    float4 hb = *reinterpret_cast<const float4*>(a.hn + c8 + 4);
+    const float* row0 = a.router_w + (int64_t)min(g, E - 1) * D + c8;
+    float4 w0 = *reinterpret_cast<const float4*>(row0);
+    float4 w1 = *reinterpret_cast<const float4*>(row0 + 4);
+    take_arrival();
+    if (!mine) ha = hb = make_float4(0.f, 0.f, 0.f, 0.f);
+    const double ss = wave_sum_dpp_f64(rms_squares8(ha, hb, 0.0));
+    if (lane == kWave - 1) s_rms[w] = ss;
+    __syncthreads();
+    const RmsScale sc = rms_scale(rms_total(s_rms), D, a.eps);
+    bool near = !sc.fast;
+    uint4 xn = rms_x8_fast(ha, hb, sc.r, near);
+    if (near) xn = rms_x8_exact(ha, hb, sc.denom);  // rare: the exact quotients
+    if (mine) reinterpret_cast<uint4*>(s_buf)[threadIdx.x] = xn;
+    uint4 xall[kMaxTok];
+#pragma unroll
+    for (int t = 0; t < kMaxTok; ++t) xall[t] = xn;
+    for (int e = g; e < E; e += G) {
+      if (e != g) {
+        const float* row = a.router_w + (int64_t)e * D + c8;
+        w0 = *reinterpret_cast<const float4*>(row);
+        w1 = *reinterpret_cast<const float4*>(row + 4);
+      }
+      double acc[kMaxTok];
+#pragma unroll
+      for (int t = 0; t < kMaxTok; ++t) acc[t] = 0.0;
+      if (mine) dot8(acc, w0, w1, xall);
+      publish_logits(e, acc);
+    }
+    if (g >= E) __syncthreads();  // the x chunks in LDS are read by other threads below
+  } else {
+    for (int e = g; e < E; e += G) {
+      const float* row = a.router_w + (int64_t)e * D;
+      double acc[kMaxTok];
+#pragma unroll
+      for (int t = 0; t < kMaxTok; ++t) acc[t] = 0.0;
+      auto chunk = [&](const int c) {
+        const float4 w0 = *reinterpret_cast<const float4*>(row + c);
+        const float4 w1 = *reinterpret_cast<const float4*>(row + c + 4);
+        uint4 xall[kMaxTok];  // every token's activations requested before the first use
+#pragma unroll
+        for (int t = 0; t < kMaxTok; ++t)
+          xall[t] = *reinterpret_cast<const uint4*>(a.x + (int64_t)min(t, B - 1) * D + c);
+        take_arrival();
+        dot8(acc, w0, w1, xall);
+      };
+      // One 8-weight chunk per thread in straight-line code when the row
+      // fits (d_model <= 4096): no loop header for the compiler to wait at.
+      if (D <= 8 * kW * kWave) {
+        if (8 * (int)threadIdx.x < D) chunk(8 * threadIdx.x);
+      } else {
+        for (int c = 8 * threadIdx.x; c < D; c += 8 * kW * kWave) chunk(c);
+      }
+      publish_logits(e, acc);
+    }
   }
   take_arrival();  // workgroups without a router row
   if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints] = t_start;
@@ -395,7 +435,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int i = threadIdx.x + q * kW * kWave;
-    if (i < B * UG) F::load_x(a.x + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);
+    if (i < B * UG) {
+      if constexpr (NORM)
+        F::load_x(reinterpret_cast<const uint16_t*>(s_buf) + (i / UG) * D, i - (i / UG) * UG, xraw[q]);
+      else
+        F::load_x(a.x + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);
+    }
   }
   stamp(a, 2);
 
@@ -1136,22 +1181,30 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
 }
 
-template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK>
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM>
 hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK>), dim3(grid), dim3(kW * kWave), 0, s, a);
+  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK, NORM>), dim3(grid), dim3(kW * kWave), 0, s,
+                     a);
   return hipGetLastError();
 }
 
-// DNK: k-steps of the matrix-core down projection (0: vector path).
-template <class F, int UPS, int DNK>
+// DNK: k-steps of the matrix-core down projection (0: vector path).  NORM
+// (the kernel normalises the residual stream itself) exists for the
+// matrix-core path only.
+template <class F, int UPS, int DNK, bool NORM = false>
 hipError_t launch_fused_f(const FusedArgs& a, int grid, int gu_units, int dn_units, hipStream_t s) {
-  if (DNK > 0) {
-    return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, DNK>(a, grid, s) : launch_fused_t<F, 1, 1, UPS, DNK>(a, grid, s);
+  if constexpr (DNK > 0) {
+    return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, DNK, NORM>(a, grid, s)
+                            : launch_fused_t<F, 1, 1, UPS, DNK, NORM>(a, grid, s);
+  } else {
+    static_assert(!NORM, "the in-kernel norm is built for the matrix-core path");
+    if (gu_units > kWave) {
+      return dn_units > kWave ? launch_fused_t<F, 2, 2, UPS, 0, false>(a, grid, s)
+                              : launch_fused_t<F, 2, 1, UPS, 0, false>(a, grid, s);
+    }
+    return dn_units > kWave ? launch_fused_t<F, 1, 2, UPS, 0, false>(a, grid, s)
+                            : launch_fused_t<F, 1, 1, UPS, 0, false>(a, grid, s);
   }
-  if (gu_units > kWave) {
-    return dn_units > kWave ? launch_fused_t<F, 2, 2, UPS, 0>(a, grid, s) : launch_fused_t<F, 2, 1, UPS, 0>(a, grid, s);
-  }
-  return dn_units > kWave ? launch_fused_t<F, 1, 2, UPS, 0>(a, grid, s) : launch_fused_t<F, 1, 1, UPS, 0>(a, grid, s);
 }
 
 template <class F>
@@ -1168,12 +1221,13 @@ hipError_t launch_fused_ups(const FusedArgs& a, int grid, int gu_units, int dn_u
 
 // MXFP4 with the down projections in MOE_LAYOUT_MFMA16 (d_ff slices of at
 // most 256 columns per XCD).
-inline hipError_t launch_fused_mfma(const FusedArgs& a, int grid, int gu_units, int ups, hipStream_t s) {
+template <bool NORM>
+hipError_t launch_fused_mfma(const FusedArgs& a, int grid, int gu_units, int ups, hipStream_t s) {
   switch (ups) {
-    case 1: return launch_fused_f<MxFmt, 1, 1>(a, grid, gu_units, 0, s);
-    case 2: return launch_fused_f<MxFmt, 2, 1>(a, grid, gu_units, 0, s);
-    case 4: return launch_fused_f<MxFmt, 4, 1>(a, grid, gu_units, 0, s);
-    case 8: return launch_fused_f<MxFmt, 8, 2>(a, grid, gu_units, 0, s);
+    case 1: return launch_fused_f<MxFmt, 1, 1, NORM>(a, grid, gu_units, 0, s);
+    case 2: return launch_fused_f<MxFmt, 2, 1, NORM>(a, grid, gu_units, 0, s);
+    case 4: return launch_fused_f<MxFmt, 4, 1, NORM>(a, grid, gu_units, 0, s);
+    case 8: return launch_fused_f<MxFmt, 8, 2, NORM>(a, grid, gu_units, 0, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1181,6 +1235,7 @@ inline hipError_t launch_fused_mfma(const FusedArgs& a, int grid, int gu_units, 
 // One instantiation set per weight format (each in its own translation unit).
 hipError_t launch_mx(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
 hipError_t launch_mx_mfma(const FusedArgs& a, int grid, int gu_units, int ups, hipStream_t s);
+hipError_t launch_mx_mfma_norm(const FusedArgs& a, int grid, int gu_units, int ups, hipStream_t s);
 hipError_t launch_q2k(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
 hipError_t launch_int4(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
 

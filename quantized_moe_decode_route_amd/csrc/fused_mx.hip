@@ -10,7 +10,7 @@ hipError_t launch_mx(const FusedArgs& a, int grid, int gu_units, int dn_units, i
 }
 
 hipError_t launch_mx_mfma(const FusedArgs& a, int grid, int gu_units, int ups, hipStream_t s) {
-  return launch_fused_mfma(a, grid, gu_units, ups, s);
+  return launch_fused_mfma<false>(a, grid, gu_units, ups, s);
 }
 
 }  // namespace fused

@@ -64,15 +64,20 @@ __global__ __launch_bounds__(kRmsThreads) void rmsnorm_kernel(const float* __res
         ss = __builtin_fma(v, v, ss);
       }
   }
-  ss = wave_sum_f64(ss);
-  if (lane_id() == 0) s_part[i / kWave] = ss;
+  ss = wave_sum_dpp_f64(ss);
+  if (lane_id() == kWave - 1) s_part[i / kWave] = ss;
   __syncthreads();
   const RmsScale sc = rms_scale(rms_total(s_part), D, eps);
   if (vec) {
-    if (8 * i < D) *reinterpret_cast<uint4*>(xo + 8 * i) = rms_x8(a, b, sc);
+    if (8 * i < D) {
+      bool near = !sc.fast;
+      uint4 x = rms_x8_fast(a, b, sc.r, near);
+      if (near) x = rms_x8_exact(a, b, sc.denom);
+      *reinterpret_cast<uint4*>(xo + 8 * i) = x;
+    }
   } else {
-    // element by element (same values as rms_x8: the fast form only ever
-    // returns the correctly rounded quotient)
+    // element by element (the same values: the fast form only ever returns
+    // the correctly rounded quotient)
     for (int c = i; 8 * c < D; c += kRmsThreads)
       for (int j = 8 * c; j < min(8 * c + 8, D); ++j) xo[j] = (uint16_t)f64_to_bf16_rne((double)row[j] / sc.denom);
   }

@@ -114,6 +114,27 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int v, int old) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_d(double v) {
+  const int lo = dpp_i<CTRL, ROW_MASK>(__double2loint(v), 0);
+  const int hi = dpp_i<CTRL, ROW_MASK>(__double2hiint(v), 0);
+  return __hiloint2double(hi, lo);
+}
+// Sum over the wave in a fixed DPP tree; the total lands in lane 63.
+__device__ __forceinline__ double wave_sum_dpp_f64(double v) {
+  v += dpp_d<0xB1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_d<0x4E>(v);        // quad_perm [2,3,0,1]
+  v += dpp_d<0x141>(v);       // row_half_mirror
+  v += dpp_d<0x140>(v);       // row_mirror
+  v += dpp_d<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_d<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // fp64 -> bfloat16 bits, round to nearest even, without double rounding:
 // first to fp32 with round-to-odd (24 >= 8 + 2 bits), then fp32 -> bf16 RNE.
 __device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
@@ -134,7 +155,7 @@ __device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
 // kernel and the single-launch layer (so their activations agree bit for
 // bit): the row is cut into 8-element chunks, thread i of 512 takes chunks
 // i, i+512, ... and adds their squares with fma in element order, each wave
-// sums its 64 lanes with the shfl-xor tree of wave_sum_f64, and the eight
+// sums its 64 lanes with the DPP tree of wave_sum_dpp_f64, and the eight
 // wave sums are added as ((w0+w1)+(w2+w3))+((w4+w5)+(w6+w7)).
 constexpr int kRmsThreads = 512;
 constexpr int kRmsWaves = kRmsThreads / kWave;
@@ -168,31 +189,34 @@ __device__ __forceinline__ RmsScale rms_scale(double total, int D, double eps) {
   return s;
 }
 
-// bf16_rne(h_j / denom) of eight elements, packed low element first.  Fast
-// form: q = RN32(h * r) lies within 1.5 fp32 ulps of the exact quotient
+// Fast form of bf16_rne(h_j / denom) for eight elements, packed low element
+// first.  q = RN32(h * r) lies within 1.5 fp32 ulps of the exact quotient
 // (one rounding in r, one in the product; in the subnormal range within one
 // ulp), so unless q's low 16 bits sit within 2 of the bf16 rounding midpoint
-// 0x8000, q and the exact quotient round to the same bfloat16, which is then
-// q's upper half after adding 0x8000 (no tie is possible).  Near a midpoint,
-// or without a fast scale, the exact fp64 quotient is rounded instead.
-__device__ __forceinline__ uint4 rms_x8(const float4& a, const float4& b, const RmsScale& s) {
+// 0x8000, q and the exact quotient round to the same bfloat16: q rounded to
+// nearest (no tie is possible).  `near` is raised otherwise; the caller then
+// takes rms_x8_exact.
+typedef float rms_f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 rms_b2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 rms_x8_fast(const float4& a, const float4& b, float r, bool& near) {
   const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t o[4];
-  bool near = !s.fast;
-  if (s.fast) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t q0 = __float_as_uint(v[2 * j] * s.r), q1 = __float_as_uint(v[2 * j + 1] * s.r);
-      near |= ((q0 + 2u - 0x8000u) & 0xFFFFu) <= 4u;
-      near |= ((q1 + 2u - 0x8000u) & 0xFFFFu) <= 4u;
-      o[j] = __builtin_amdgcn_perm(q1 + 0x8000u, q0 + 0x8000u, 0x07060302u);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const rms_f2 q = {v[2 * j] * r, v[2 * j + 1] * r};
+    near |= (uint16_t)(__float_as_uint(q.x) - 0x7FFEu) <= 4u;
+    near |= (uint16_t)(__float_as_uint(q.y) - 0x7FFEu) <= 4u;
+    o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(q, rms_b2));
   }
-  if (near) {
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+// bf16_rne of the exact fp64 quotients.
+__device__ __forceinline__ uint4 rms_x8_exact(const float4& a, const float4& b, double denom) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t o[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      o[j] = f64_to_bf16_rne((double)v[2 * j] / s.denom) | (f64_to_bf16_rne((double)v[2 * j + 1] / s.denom) << 16);
-  }
+  for (int j = 0; j < 4; ++j)
+    o[j] = f64_to_bf16_rne((double)v[2 * j] / denom) | (f64_to_bf16_rne((double)v[2 * j + 1] / denom) << 16);
   return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
@@ -324,9 +348,13 @@ FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx, in
 // yet, -1 placement unsuitable for the single-launch layer, else the count.
 int probe_xcd_count(uint32_t* scratch, int grid, hipStream_t s);
 int xcd_count();
-hipError_t launch_fused_layer(int fmt, const float* router_w, const uint16_t* x, const WeightRef& gate,
-                              const WeightRef& up, const WeightRef& down, int E, int D, int Fd, int k, int B,
-                              uint8_t* ws, const WsLayout& L, float* y, const float* residual, int32_t* idx_out,
-                              float* gw_out, uint64_t* trace, hipStream_t s);
+// x: bf16 activations [B][D]; or, with hn set (x unused), the residual
+// stream fp32 [1][D] of one token that the kernel RMS-normalises itself
+// (B = 1, D <= 4096, D % 8 == 0, matrix-core layout; hn must not alias y).
+hipError_t launch_fused_layer(int fmt, const float* router_w, const uint16_t* x, const float* hn, double eps,
+                              const WeightRef& gate, const WeightRef& up, const WeightRef& down, int E, int D, int Fd,
+                              int k, int B, uint8_t* ws, const WsLayout& L, float* y, const float* residual,
+                              int32_t* idx_out, float* gw_out, uint64_t* trace, hipStream_t s);
+constexpr int kFusedNormMaxD = 4096;
 
 }  // namespace moe

@@ -108,6 +108,40 @@ def test_stack_teacher_forced(B):
     assert np.array_equal(host(hout), hs[-1])
 
 
+@pytest.mark.parametrize("fmt,layout,B,D,F,E", [
+    ("mxfp4", "mfma16", 1, 512, 256, 32), ("mxfp4", "mfma16", 1, 4096, 2048, 256),
+    ("mxfp4", "mfma16", 1, 992, 256, 32), ("mxfp4", "rows", 1, 512, 256, 32),
+    ("q2k", "rows", 8, 512, 256, 32), ("mxfp4", "mfma16", 8, 4096, 2048, 256)])
+def test_stack_in_kernel_norm_matches_norm_kernel(fmt, layout, B, D, F, E):
+    """A one-token stack step with the MXFP4 matrix-core layer normalises its
+    input inside the single-launch layer kernel; run in place (h_out aliasing
+    h_in) with one layer, the separate norm kernel does it instead.  Both
+    define the same sum order and the same rounding, so the residual states
+    agree bit for bit.  (The other cases take the norm kernel both ways.)"""
+    layers = [Layer(fmt, 0x5EED + 40 + B, l, E, D, F, 6, down_layout=layout) for l in range(2)]
+    h = synth.f32_from_bf16_bits(synth.token_bf16(4100 + B, B, D)) * np.float32(3.0)
+    ws = torch.empty(moe.moe_stack_workspace_bytes(B, D, F, E, 6), dtype=torch.uint8, device="cuda")
+    moe.moe_workspace_init(ws)
+    for l in range(2):
+        hin = dev(h)
+        hout = torch.empty_like(hin)
+        moe.moe_stack_decode([layers[l].desc], hin, hout, ws)       # in-kernel norm
+        inplace = dev(h)
+        moe.moe_stack_decode([layers[l].desc], inplace, inplace, ws)  # norm kernel, then the layer
+        torch.cuda.synchronize()
+        a, b = host(hout), host(inplace)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"layer {l}"
+        h = a
+    # two layers in one call (each normalising in-kernel) give the same bits
+    hin = dev(synth.f32_from_bf16_bits(synth.token_bf16(4100 + B, B, D)) * np.float32(3.0))
+    hout = torch.empty_like(hin)
+    moe.moe_stack_decode([L.desc for L in layers], hin, hout, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(hout).view(np.uint32), h.view(np.uint32))
+    del layers
+    torch.cuda.empty_cache()
+
+
 def test_stack_full_shape_three_layers():
     D, F, E = 4096, 2048, 256
     layers = [Layer("mxfp4", 0x5EED + 4, l, E, D, F, 6) for l in range(3)]
