@@ -251,6 +251,8 @@ struct Rings<Int4Fmt> {  // its gate/up unpacking keeps more registers live
   static constexpr int kDN = 6;
 };
 constexpr int kSpinBatch = 12;  // tagged words a thread reads before its first wait
+constexpr int kPrefetchExperts = 1;  // one token: experts whose gate/up rows go to L2 during top-k
+constexpr bool kPrefetchDown = true;  // ... and their down rows
 
 template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM>
 __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a) {
@@ -278,13 +280,14 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 
   __shared__ int32_t s_idx[kMaxSlots];
   __shared__ float s_gw[kMaxSlots];
-  __shared__ LayerGroup s_grp[kMaxSlots];
+  __shared__ LayerGroup s_grp[kW][kMaxSlots];  // one group table per wave
   __shared__ uint32_t s_mask[MOE_MAX_EXPERTS];  // per expert: tokens that picked it and at which rank
   __shared__ double s_part[kW][kMaxTok];
   __shared__ double s_rms[kW];  // in-kernel norm: the waves' sums of squares
   __shared__ int s_next;                 // matrix-core path: next token slot to gather
   __shared__ int s_gu_next;              // next gate/up work item
-  __shared__ int s_U;
+  __shared__ int s_pre[kMaxSlots];       // one token: experts in the order the top-k finds them
+  __shared__ int s_pre_n;                // ... and how many are known
   __shared__ int s_timeout;
   __shared__ int s_jx;
   __shared__ __align__(16) uint8_t s_buf[kLdsBytes];
@@ -310,6 +313,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   if (threadIdx.x == 0) {
     s_next = 0;
     s_gu_next = 0;
+    s_pre_n = 0;
   }
 
   const int UG = F::units(D);
@@ -531,6 +535,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         my_v = bv;
         my_i = bi;
       }
+      if (B == 1 && lane == 0) {  // for the prefetching waves
+        reinterpret_cast<volatile int*>(s_pre)[r] = min(max(bi, 0), E - 1);
+        *reinterpret_cast<volatile int*>(&s_pre_n) = r + 1;
+      }
       if (id[0] == bi) {  // this lane held the winner: pop it
         v[0] = v[1];
         id[0] = id[1];
@@ -558,21 +566,44 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       atomicOr(&s_mask[my_i], (1u << t) | ((uint32_t)lane << (8 + 3 * t)));
     }
   }
-  __syncthreads();
-  stamp(a, 4);
-  // Group (token, rank) pairs by expert, experts ascending: one record per
-  // selected expert holding its packed token mask.
-  if (w == 0) {
-    int base = 0;
-#pragma unroll
-    for (int q = 0; q < MOE_MAX_EXPERTS / kWave; ++q) {
-      const int ex = q * kWave + lane;
-      const uint32_t mask = ex < E ? s_mask[ex] : 0u;
-      const uint64_t used = __ballot(mask != 0u);
-      if (mask != 0u) s_grp[base + __popcll(used & ((1ull << lane) - 1ull))] = LayerGroup{ex, mask};
-      base += __popcll(used);
+  // One token: while wave 0 selects the experts, the other waves pull this
+  // workgroup's gate/up rows of the first ones into the XCD's L2 (taking the
+  // workgroup's likely place in the XCD from its index: a wrong guess only
+  // prefetches another workgroup's rows), so the first gate/up loads find
+  // them there.  The loaded bytes are kept until after gate/up, whose waits
+  // cover these older loads anyway.
+  uint32_t pre_sink = 0u;
+  if constexpr (std::is_same<F, MxFmt>::value) {
+    if (B == 1 && w >= 1) {
+      const int FSp = Fd / NX, RPWp = (FSp + GX - 1) / GX;
+      const int fr = xcd * FSp + ((int)(blockIdx.x / NX) % GX) * RPWp;
+      const int rows = min(RPWp, xcd * FSp + FSp - fr);
+      const int64_t rb = (int64_t)(D / 32) * 17;  // bytes per row
+      const int64_t nbytes = rows > 0 ? rows * rb : 0;
+      const int lines = (int)((nbytes + 127) / 128);
+      const int p = (int)threadIdx.x - kWave;
+      const uint64_t t0 = wall_clock64();
+      for (int r = 0; r < min(k, kPrefetchExperts) && lines > 0; ++r) {
+        while (*reinterpret_cast<volatile int*>(&s_pre_n) <= r && wall_clock64() - t0 < kSpinTicks)
+          __builtin_amdgcn_s_sleep(1);
+        const int e = reinterpret_cast<volatile int*>(s_pre)[r];
+        if (p < 2 * lines) {
+          const WeightRef& m = p < lines ? a.gate : a.up;
+          const int64_t off = min((int64_t)(p < lines ? p : p - lines) * 128, nbytes - 1);
+          pre_sink += m.base[e * m.stride + fr * rb + off];
+        } else if (kPrefetchDown && DNK == 2 && a.down.layout == MOE_LAYOUT_MFMA16 && Fd / NX == 256) {
+          // the expert's down blocks of this slice for the workgroup's output
+          // rows: one contiguous run in the MOE_LAYOUT_MFMA16 order
+          const int RPWdp = (D + GX - 1) / GX;
+          const int nd0 = ((int)(blockIdx.x / NX) % GX) * RPWdp;
+          const int q = p - 2 * lines;
+          if (RPWdp % 16 == 0 && nd0 + RPWdp <= D && q * 128 < RPWdp * 8 * 17) {
+            const int64_t blk = mfma16_block(nd0, xcd * 8, D);
+            pre_sink += a.down.base[e * a.down.stride + blk * 17 + q * 128];
+          }
+        }
+      }
     }
-    if (lane == 0) s_U = base;
   }
   if (threadIdx.x == 0) {  // the arrival counter has long returned by now
     s_jx = (int)(xcd_arrival % (uint32_t)GX);
@@ -581,9 +612,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       a.trace[blockIdx.x * kTracePoints + kTracePoints - 1] = (uint64_t)xcd_arrival;
     }
   }
-  // Stage the activations.  They are opaque until here, so the compiler
-  // cannot hoist their rearrangement into the routing, where it would wait
-  // for x.
+  // Stage the activations (their loads have long returned: the logit reads
+  // above were issued after them).  They are opaque until here, so the
+  // compiler cannot hoist their rearrangement into the routing, where it
+  // would wait for x.
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -608,17 +640,35 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     if (threadIdx.x < 4 * DNK) hb0[(size_t)(S + 1) * DNK * 512 + S * 4 * DNK + threadIdx.x] = 0;
   }
   __syncthreads();
-  const int U = s_U;
-  // The group table, one group per lane (U <= kMaxSlots = 64): the rings read
-  // an expert or a token mask with v_readlane instead of an LDS round trip.
-  // For the matrix-core down projection, the slots of the group's tokens in
-  // ascending token order, one byte each (tokens 0..3 in gsl_lo, 4..7 in
-  // gsl_hi).
+  stamp(a, 4);
+  // Group (token, rank) pairs by expert, experts ascending: one record per
+  // selected expert holding its packed token mask.  Every wave builds the
+  // table itself (in its own LDS row, read back by the same wave), so no
+  // second barrier is needed.  The group table, one group per lane (U <=
+  // kMaxSlots = 64): the rings read an expert or a token mask with
+  // v_readlane instead of an LDS round trip.  For the matrix-core down
+  // projection, the slots of the group's tokens in ascending token order,
+  // one byte each (tokens 0..3 in gsl_lo, 4..7 in gsl_hi).
   static_assert(kMaxSlots <= kWave, "one group per lane");
+  int U = 0;
   int g_exp;
   uint32_t g_mask, gsl_lo = 0u, gsl_hi = 0u;  // slot tables: filled after gate/up
-  {
-    const LayerGroup gr = s_grp[min(lane, U - 1)];
+  if (B == 1) {  // one token: the groups in rank order (the order of the prefetch)
+    U = k;
+    const int r = min(lane, k - 1);
+    g_exp = s_idx[r];
+    g_mask = 1u | ((uint32_t)r << 8);
+  } else {
+#pragma unroll
+    for (int q = 0; q < MOE_MAX_EXPERTS / kWave; ++q) {
+      const int ex = q * kWave + lane;
+      const uint32_t mask = ex < E ? s_mask[ex] : 0u;
+      const uint64_t used = __ballot(mask != 0u);
+      if (mask != 0u) s_grp[w][U + __popcll(used & ((1ull << lane) - 1ull))] = LayerGroup{ex, mask};
+      U += __popcll(used);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const LayerGroup gr = s_grp[w][min(lane, U - 1)];
     g_exp = gr.expert;
     g_mask = gr.mask;
   }
@@ -1048,6 +1098,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     while (item[kRingGU - 1] < NI) pass(std::false_type{});
   }
   stamp(a, 6);
+  asm volatile("" ::"v"(pre_sink));  // the prefetched bytes, long since arrived
   fill_slot_tables();
 
   // ---------------------------------------------------------------- 3. down (partials over the slice)
