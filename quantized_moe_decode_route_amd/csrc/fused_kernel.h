@@ -786,9 +786,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // operand: four fp8 (E4M3) terms per value under one E8M0 exponent per 32
   // values.  With every group's down weights already in the prologue slots
   // (U <= kRingDN - 1) the down projection is a plain loop over the groups.
-  constexpr int kGatherBatch = 3;
   const bool dn_walk = U <= kRingDN - 1;
-  auto gather_batch = [&]() -> bool {  // false once every slot is claimed
+  // kGatherBatch slots per claim (3; 1 when there are no more slots than
+  // waves, so that every slot is converted by a wave of its own).
+  auto gather_batch = [&](auto nb) -> bool {  // false once every slot is claimed
+    constexpr int kGatherBatch = decltype(nb)::value;
     int i0 = 0;
     if (lane == 0) i0 = atomicAdd(&s_next, kGatherBatch);
     i0 = __builtin_amdgcn_readfirstlane(i0);
@@ -1145,7 +1147,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   if constexpr (DNK > 0) {
     __syncthreads();  // every row of this workgroup is published
     stamp(a, 11);
-    while (gather_batch()) {
+    if (S <= kW) {
+      while (gather_batch(std::integral_constant<int, 1>{})) {
+      }
+    } else {
+      while (gather_batch(std::integral_constant<int, 3>{})) {
+      }
     }
     stamp(a, 12);
     if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints + 13] = (uint64_t)trace_rereads;
