@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 enum moe_status {
   MOE_OK = 0,
@@ -144,7 +144,7 @@ int moe_route_topk(const float* router_w, int E, int D, const uint16_t* x_bf16, 
  * in the W4A16 model card's quantization scheme.
  */
 typedef struct moe_layer_desc {
-  int format;        /* enum moe_format, all three projections */
+  int format;        /* enum moe_format of gate and up (and of down unless down_format says otherwise) */
   int n_experts;     /* E <= 256 */
   int d_model;       /* D: multiple of 256 for Q2_K, of 32 otherwise */
   int d_ff;          /* F: same constraint */
@@ -163,7 +163,16 @@ typedef struct moe_layer_desc {
   int64_t gate_scale_stride, up_scale_stride, down_scale_stride;
   int down_layout;   /* enum moe_layout of every expert's down projection
                       * (and of its INT4 scales); gate and up are row-major */
+  /* Per-tensor-family precision ("Mixed-precision compression of
+   * DeepSeek-V4-Flash", "The recipe": routed gate/up at 2 bits, down at
+   * Q2_K): 0 = down in `format` like gate and up; otherwise 1 + the enum
+   * moe_format of the down projection (then `format` covers gate and up,
+   * down_scale is used only for an INT4G32 down, and d_ff must suit both
+   * formats' block lengths).  A zeroed field keeps every projection in
+   * `format`. */
+  int down_format;
 } moe_layer_desc;
+enum moe_down_format { MOE_DOWN_SAME = 0, MOE_DOWN_MXFP4 = 1, MOE_DOWN_Q2K = 2, MOE_DOWN_INT4G32 = 3 };
 
 /* Workspace for moe_layer_decode with up to B tokens (256-byte aligned). */
 size_t moe_layer_workspace_bytes(int B, int D, int F, int E, int top_k);

@@ -268,18 +268,23 @@ def rmsnorm_bf16(h: np.ndarray, eps: float = 1e-6) -> np.ndarray:
 
 # ---------------------------------------------------------------- expert FFN / layer
 
-def expert_ffn(fmt: str, gate, up, down, x: np.ndarray, d_model: int, d_ff: int) -> np.ndarray:
-    """One routed expert on one or more tokens: down(silu(gate x) * (up x)), fp64."""
+def expert_ffn(fmt, gate, up, down, x: np.ndarray, d_model: int, d_ff: int) -> np.ndarray:
+    """One routed expert on one or more tokens: down(silu(gate x) * (up x)), fp64.
+
+    ``fmt``: one format for all three projections, or (gate/up format, down
+    format): precision is assigned per tensor family ("Mixed-precision
+    compression of DeepSeek-V4-Flash", "The recipe")."""
+    fg, fd = (fmt, fmt) if isinstance(fmt, str) else fmt
     xx = np.asarray(x, dtype=np.float64).reshape(-1, d_model)
-    gv = gemv(fmt, gate, d_ff, d_model, xx)
-    uv = gemv(fmt, up, d_ff, d_model, xx)
+    gv = gemv(fg, gate, d_ff, d_model, xx)
+    uv = gemv(fg, up, d_ff, d_model, xx)
     h = silu_mul(gv, uv)
-    return gemv(fmt, down, d_model, d_ff, h)
+    return gemv(fd, down, d_model, d_ff, h)
 
 
-def layer_decode(fmt: str, get_expert, wr: np.ndarray, x_bf16: np.ndarray, top_k: int = 6,
+def layer_decode(fmt, get_expert, wr: np.ndarray, x_bf16: np.ndarray, top_k: int = 6,
                  d_ff: int | None = None):
-    """One MoE layer for B tokens.
+    """One MoE layer for B tokens (``fmt`` as in ``expert_ffn``).
 
     ``get_expert(e)`` returns ``(gate, up, down)`` weights of expert ``e``.
     Returns ``(y fp64 [B, D], idx int32 [B, k], g fp64 [B, k])``.
@@ -302,7 +307,7 @@ def layer_decode(fmt: str, get_expert, wr: np.ndarray, x_bf16: np.ndarray, top_k
     return y, idx, g
 
 
-def stack_decode(fmt: str, get_layer_expert, routers, x_bf16: np.ndarray, top_k: int = 6,
+def stack_decode(fmt, get_layer_expert, routers, x_bf16: np.ndarray, top_k: int = 6,
                  d_ff: int | None = None, eps: float = 1e-6, trace: bool = False):
     """Residual stream through ``len(routers)`` layers: x_l = bf16(rmsnorm(h_l)),
     h_{l+1} = h_l + moe_l(x_l), h_0 = x (the activation's exact value).

@@ -20,7 +20,7 @@ FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2k": MOE_FMT_Q2K, "int4g32": MOE_FMT_INT4G3
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE256, MOE_LAYOUT_MFMA16 = 0, 1, 2
 LAYOUTS = {"rows": MOE_LAYOUT_ROWS, "tile256": MOE_LAYOUT_TILE256, "mfma16": MOE_LAYOUT_MFMA16}
 # MOE_ABI_VERSION of include/moe_decode.h that this binding is written for
-ABI_VERSION = 3
+ABI_VERSION = 4
 MOE_MAX_TOKENS = 8
 MOE_MAX_TOPK = 8
 
@@ -54,7 +54,7 @@ class moe_layer_desc(ctypes.Structure):
         ("gate_scale", ctypes.c_void_p), ("up_scale", ctypes.c_void_p), ("down_scale", ctypes.c_void_p),
         ("gate_scale_stride", ctypes.c_int64), ("up_scale_stride", ctypes.c_int64),
         ("down_scale_stride", ctypes.c_int64),
-        ("down_layout", ctypes.c_int),
+        ("down_layout", ctypes.c_int), ("down_format", ctypes.c_int),
     ]
 
 
@@ -182,10 +182,12 @@ def moe_workspace_init(ws, stream=None) -> None:
 def make_layer_desc(fmt: str, router_w, gate, up, down, n_experts: int, d_model: int, d_ff: int, top_k: int,
                     gate_stride: int, up_stride: int, down_stride: int, gate_scale=None, up_scale=None,
                     down_scale=None, gate_scale_stride: int = 0, up_scale_stride: int = 0,
-                    down_scale_stride: int = 0, down_layout: str = "rows") -> moe_layer_desc:
+                    down_scale_stride: int = 0, down_layout: str = "rows",
+                    down_format: str | None = None) -> moe_layer_desc:
     """Fill the C descriptor; tensors (or raw device addresses) must outlive its use.
     ``down_layout``: "rows" (as published), "tile256" (see moe_tile_weights) or
-    "mfma16" (MXFP4 only, see moe_tile_weights_mfma16)."""
+    "mfma16" (MXFP4 only, see moe_tile_weights_mfma16).  ``down_format``: the
+    down projection's format when it differs from ``fmt`` (gate and up)."""
     d = moe_layer_desc()
     d.format = FORMATS[fmt]
     d.n_experts, d.d_model, d.d_ff, d.top_k = n_experts, d_model, d_ff, top_k
@@ -195,6 +197,7 @@ def make_layer_desc(fmt: str, router_w, gate, up, down, n_experts: int, d_model:
     d.gate_scale, d.up_scale, d.down_scale = _ptr(gate_scale), _ptr(up_scale), _ptr(down_scale)
     d.gate_scale_stride, d.up_scale_stride, d.down_scale_stride = gate_scale_stride, up_scale_stride, down_scale_stride
     d.down_layout = LAYOUTS[down_layout]
+    d.down_format = 0 if down_format is None or down_format == fmt else 1 + FORMATS[down_format]
     return d
 
 

@@ -45,30 +45,42 @@ int check_gemv(const void* w, int N, int K, const float* x, int B, float* y, int
   return MOE_OK;
 }
 
+// Format of the down projection (enum moe_format), or -1 if invalid.
+int down_fmt(const moe_layer_desc* L) {
+  if (L->down_format == MOE_DOWN_SAME) return L->format;
+  if (L->down_format < MOE_DOWN_MXFP4 || L->down_format > MOE_DOWN_INT4G32) return -1;
+  return L->down_format - 1;
+}
+
 int check_layer(const moe_layer_desc* L, int B) {
   if (!L) return MOE_ERR_ARG;
-  if (L->format < MOE_FMT_MXFP4 || L->format > MOE_FMT_INT4G32) return MOE_ERR_ARG;
+  const int fg = L->format, fd = down_fmt(L);
+  if (fg < MOE_FMT_MXFP4 || fg > MOE_FMT_INT4G32 || fd < 0) return MOE_ERR_ARG;
   if (!L->router_w || !L->gate || !L->up || !L->down) return MOE_ERR_ARG;
   if (L->n_experts < 1 || L->n_experts > MOE_MAX_EXPERTS) return MOE_ERR_SHAPE;
   if (L->top_k < 1 || L->top_k > MOE_MAX_TOPK || L->top_k > L->n_experts) return MOE_ERR_SHAPE;
   if (B < 1 || B > MOE_MAX_TOKENS) return MOE_ERR_SHAPE;
-  const int bl = block_len(L->format);
+  const int bl = block_len(fg) > block_len(fd) ? block_len(fg) : block_len(fd);
   if (L->d_model <= 0 || L->d_ff <= 0 || L->d_model % bl || L->d_ff % bl) return MOE_ERR_SHAPE;
   if (L->gate_stride < 0 || L->up_stride < 0 || L->down_stride < 0) return MOE_ERR_ARG;
   if (!aligned(L->router_w, 16)) return MOE_ERR_ALIGN;
-  const uintptr_t wa = L->format == MOE_FMT_INT4G32 ? 16 : 4;
-  if (!aligned(L->gate, wa) || !aligned(L->up, wa) || !aligned(L->down, wa)) return MOE_ERR_ALIGN;
-  if (L->gate_stride % wa || L->up_stride % wa || L->down_stride % wa) return MOE_ERR_ALIGN;
+  const uintptr_t wg = fg == MOE_FMT_INT4G32 ? 16 : 4, wd = fd == MOE_FMT_INT4G32 ? 16 : 4;
+  if (!aligned(L->gate, wg) || !aligned(L->up, wg) || !aligned(L->down, wd)) return MOE_ERR_ALIGN;
+  if (L->gate_stride % wg || L->up_stride % wg || L->down_stride % wd) return MOE_ERR_ALIGN;
   if (L->down_layout != MOE_LAYOUT_ROWS && L->down_layout != MOE_LAYOUT_TILE256 &&
       L->down_layout != MOE_LAYOUT_MFMA16)
     return MOE_ERR_ARG;
-  if (L->down_layout == MOE_LAYOUT_MFMA16 && L->format != MOE_FMT_MXFP4) return MOE_ERR_ARG;
+  if (L->down_layout == MOE_LAYOUT_MFMA16 && fd != MOE_FMT_MXFP4) return MOE_ERR_ARG;
   if (L->down_layout != MOE_LAYOUT_ROWS && L->d_ff % kTileCols) return MOE_ERR_SHAPE;
   if (L->down_layout == MOE_LAYOUT_MFMA16 && L->d_model % 16) return MOE_ERR_SHAPE;
-  if (L->format == MOE_FMT_INT4G32) {
-    if (!L->gate_scale || !L->up_scale || !L->down_scale) return MOE_ERR_ARG;
-    if (!aligned(L->gate_scale, 2) || !aligned(L->up_scale, 2) || !aligned(L->down_scale, 2)) return MOE_ERR_ALIGN;
-    if (L->gate_scale_stride % 2 || L->up_scale_stride % 2 || L->down_scale_stride % 2) return MOE_ERR_ALIGN;
+  if (fg == MOE_FMT_INT4G32) {
+    if (!L->gate_scale || !L->up_scale) return MOE_ERR_ARG;
+    if (!aligned(L->gate_scale, 2) || !aligned(L->up_scale, 2)) return MOE_ERR_ALIGN;
+    if (L->gate_scale_stride % 2 || L->up_scale_stride % 2) return MOE_ERR_ALIGN;
+  }
+  if (fd == MOE_FMT_INT4G32) {
+    if (!L->down_scale) return MOE_ERR_ARG;
+    if (!aligned(L->down_scale, 2) || L->down_scale_stride % 2) return MOE_ERR_ALIGN;
   }
   return MOE_OK;
 }
@@ -104,7 +116,8 @@ int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
   const int grid = fused_grid_size();
   int nx = xcd_count();
   if (nx == 0) nx = probe_xcd_count(reinterpret_cast<uint32_t*>(w + W.topo), grid, s);
-  const FusedShape sh = nx > 0 ? fused_shape(L->format, B, k, D, F, grid, nx, L->down_layout) : FusedShape{};
+  const int fd = down_fmt(L);
+  const FusedShape sh = nx > 0 ? fused_shape(L->format, fd, B, k, D, F, grid, nx, L->down_layout) : FusedShape{};
   const bool fused = nx > 0 && sh.ok;
   // In-kernel norm for one token only: at B = 8 its redundant per-workgroup
   // work (every workgroup normalises the whole batch) costs more than the
@@ -115,14 +128,14 @@ int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
     hn = nullptr;
   }
   if (fused) {
-    e = launch_fused_layer(L->format, L->router_w, x_bf16, hn, eps, g, u, d, E, D, F, k, B, w, W, y, residual,
+    e = launch_fused_layer(L->format, fd, L->router_w, x_bf16, hn, eps, g, u, d, E, D, F, k, B, w, W, y, residual,
                            idx_out, gw_out, trace, s);
     if (e != hipSuccess) return hip_status(e);
   } else {
     if ((e = launch_route(L->router_w, E, D, x_bf16, B, k, w, W, idx_out, gw_out, nullptr, s)) != hipSuccess)
       return hip_status(e);
     if ((e = launch_gate_up(L->format, g, u, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
-    if ((e = launch_down(L->format, d, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
+    if ((e = launch_down(fd, d, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
     if ((e = launch_combine(D, B, k, w, W, y, residual, s)) != hipSuccess) return hip_status(e);
   }
   if ((e = rec(1)) != hipSuccess) return hip_status(e);
@@ -258,7 +271,8 @@ int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int
   if ((st = arch_check()) != MOE_OK) return st;
   const int grid = fused_grid_size();
   const int nx = xcd_count();
-  const bool fused = nx > 0 && fused_shape(L->format, B, L->top_k, L->d_model, L->d_ff, grid, nx, L->down_layout).ok;
+  const bool fused =
+      nx > 0 && fused_shape(L->format, down_fmt(L), B, L->top_k, L->d_model, L->d_ff, grid, nx, L->down_layout).ok;
   *trace_blocks = fused ? grid : 0;
   if (!trace) return MOE_OK;  // size query
   return layer_impl(L, x_bf16, B, y, nullptr, ws, nullptr, nullptr, nullptr, (hipStream_t)stream, trace);

@@ -22,19 +22,22 @@ __global__ __launch_bounds__(kW * kWave, 1) void xcc_map_kernel(uint32_t* out) {
 
 }  // namespace
 
-FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx, int down_layout) {
+FusedShape fused_shape(int fmt, int dfmt, int B, int k, int D, int F, int grid, int nx, int down_layout) {
   FusedShape sh{};
   sh.ok = false;
   sh.mfma = down_layout == MOE_LAYOUT_MFMA16;
-  if (sh.mfma && fmt != MOE_FMT_MXFP4) return sh;
+  if (sh.mfma && (fmt != MOE_FMT_MXFP4 || dfmt != MOE_FMT_MXFP4)) return sh;
+  // mixed formats: gate/up in MXFP4 or INT4 with a Q2_K down projection
+  if (dfmt != fmt && !(dfmt == MOE_FMT_Q2K && (fmt == MOE_FMT_MXFP4 || fmt == MOE_FMT_INT4G32))) return sh;
   if (grid <= 0 || nx <= 0 || nx > kMaxNX || grid % nx) return sh;
-  const int uw = fmt == MOE_FMT_Q2K ? 64 : 32;
+  const int uwg = fmt == MOE_FMT_Q2K ? 64 : 32;   // unit width of gate/up (along d_model)
+  const int uw = dfmt == MOE_FMT_Q2K ? 64 : 32;   // unit width of down (along d_ff)
   const int gx = grid / nx;
   if (F % (nx * uw)) return sh;  // every XCD's d_ff slice is whole units
   const int ups = F / nx / uw;
   if (ups != 1 && ups != 2 && ups != 4 && ups != 8 && ups != 16) return sh;
-  sh.gu_units = D / uw;
-  if (D % uw || sh.gu_units > 2 * kWave) return sh;
+  sh.gu_units = D / uwg;
+  if (D % uwg || sh.gu_units > 2 * kWave) return sh;
   const int rpwd = (D + gx - 1) / gx;
   const int rpv = (rpwd + kW - 1) / kW;
   sh.dn_units = rpv * ups;
@@ -42,7 +45,7 @@ FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx, in
   sh.ups = ups;
   // LDS: activations during gate/up, then h slices and row partials.
   const size_t staged = fmt == MOE_FMT_Q2K ? 4 * Q2kFmt::kXDw : fmt == MOE_FMT_INT4G32 ? 4 * Int4Fmt::kXDw : 4 * MxFmt::kXDw;
-  const size_t act = (size_t)B * (D / uw) * staged;
+  const size_t act = (size_t)B * (D / uwg) * staged;
   size_t down = (size_t)B * k * ups * (uw + 4) * 4 + (size_t)B * k * rpwd * 4;
   if (sh.mfma) {
     // one 16-row tile per wave, at most two 128-column k-steps per XCD
@@ -105,7 +108,7 @@ int probe_xcd_count(uint32_t* scratch, int grid, hipStream_t s) {
   return nx = n;
 }
 
-hipError_t launch_fused_layer(int fmt, const float* router_w, const uint16_t* x, const float* hn, double eps,
+hipError_t launch_fused_layer(int fmt, int dfmt, const float* router_w, const uint16_t* x, const float* hn, double eps,
                               const WeightRef& gate, const WeightRef& up, const WeightRef& down, int E, int D, int Fd,
                               int k, int B, uint8_t* ws, const WsLayout& L, float* y, const float* residual,
                               int32_t* idx_out, float* gw_out, uint64_t* trace, hipStream_t s) {
@@ -133,8 +136,13 @@ hipError_t launch_fused_layer(int fmt, const float* router_w, const uint16_t* x,
   a.B = B;
   a.nx = xcd_count();
   const int grid = fused_grid_size();
-  const FusedShape sh = fused_shape(fmt, B, k, D, Fd, grid, a.nx, down.layout);
+  const FusedShape sh = fused_shape(fmt, dfmt, B, k, D, Fd, grid, a.nx, down.layout);
   if (!sh.ok) return hipErrorInvalidValue;
+  if (dfmt != fmt) {
+    if (hn) return hipErrorInvalidValue;
+    return fmt == MOE_FMT_MXFP4 ? fused::launch_mx_q2k(a, grid, sh.gu_units, sh.dn_units, sh.ups, s)
+                                : fused::launch_int4_q2k(a, grid, sh.gu_units, sh.dn_units, sh.ups, s);
+  }
   if (sh.mfma) {
     return hn ? fused::launch_mx_mfma_norm(a, grid, sh.gu_units, sh.ups, s)
               : fused::launch_mx_mfma(a, grid, sh.gu_units, sh.ups, s);

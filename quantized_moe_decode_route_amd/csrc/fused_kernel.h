@@ -254,11 +254,12 @@ constexpr int kSpinBatch = 12;  // tagged words a thread reads before its first 
 constexpr int kPrefetchExperts = 1;  // one token: experts whose gate/up rows go to L2 during top-k
 constexpr bool kPrefetchDown = true;  // ... and their down rows
 
-template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM>
+// F: format of gate and up; FD: format of down.
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD>
 __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a) {
   constexpr int kCh = F::kXDw / 4;  // 16-byte chunks of one unit's staged activations
   constexpr int kRingGU = Rings<F>::kGU;
-  constexpr int kRingDN = Rings<F>::kDN;
+  constexpr int kRingDN = Rings<FD>::kDN;
   const int G = gridDim.x;
   const int g = blockIdx.x;
   const int w = threadIdx.x / kWave;
@@ -707,7 +708,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // LDS views: h slice per slot, unit blocks padded by 4 floats (conflict-free
   // float4 reads; Q2_K keeps its sub-block sums there), then the per-slot row
   // partials.
-  constexpr int kHB = F::kUnitW + 4;
+  constexpr int kHB = FD::kUnitW + 4;
   float* sh = reinterpret_cast<float*>(s_buf);  // [S][UPS][kHB]
   const int RPWd = (D + GX - 1) / GX;            // output rows per workgroup
   const int RPV = (RPWd + kW - 1) / kW;          // rows per wave
@@ -728,7 +729,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // Where this lane's down unit lives: unit xcd*UPS + ub of row n, or, in
   // the tiled layout, unit (xcd*UPS + ub) % UPT of row c*D + n of the
   // [(Fd/256)*D][256] matrix, c = (xcd*UPS + ub) / UPT.
-  constexpr int UPT = kTileCols / F::kUnitW;
+  constexpr int UPT = kTileCols / FD::kUnitW;
   const bool tiled = a.down.layout == MOE_LAYOUT_TILE256;
   const int du_row = xcd * UPS + ub;
   const int dunit = tiled ? du_row % UPT : du_row;
@@ -752,18 +753,18 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     dblk[ks] = dok[ks] ? (int)mfma16_block(n0 + drl, xcd * UPS + 4 * ks + mg, D) : 0;
   }
   constexpr int kDnSlot = DNK > 0 ? DNK : MAXU_DN;
-  typename F::Raw dring[kRingDN][kDnSlot];
+  typename FD::Raw dring[kRingDN][kDnSlot];
   // Slots past the last expert load this XCD's first h words instead: the
   // h gather has just read them, so the final waits of the ring are cache
   // hits rather than trips to another XCD's weights.
   const uint8_t* hot = reinterpret_cast<const uint8_t*>(ht + f0);
-  auto load_dn = [&](int uu, typename F::Raw(&dst)[kDnSlot]) {
+  auto load_dn = [&](int uu, typename FD::Raw(&dst)[kDnSlot]) {
     const bool live = uu < U;
     const int ex = grp_expert(live ? uu : U - 1);
     if constexpr (DNK > 0) {
-      const typename F::Row all{live ? a.down.base + ex * a.down.stride : hot};
+      const typename FD::Row all{live ? a.down.base + ex * a.down.stride : hot};
 #pragma unroll
-      for (int ks = 0; ks < DNK; ++ks) F::load(all, live ? dblk[ks] : 0, dst[ks]);
+      for (int ks = 0; ks < DNK; ++ks) FD::load(all, live ? dblk[ks] : 0, dst[ks]);
     } else {
       const uint16_t* ds = a.down.scale ? reinterpret_cast<const uint16_t*>(
                                               reinterpret_cast<const uint8_t*>(a.down.scale) + ex * a.down.scale_stride)
@@ -773,10 +774,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         const int v = lane + kWave * j;
         const int rloc = w * RPV + v / UPS;
         const bool ok = live && v < UD && rloc < RPWd && n0 + rloc < D;
-        const typename F::Row rw =
-            live ? F::row(a.down.base + ex * a.down.stride, ds, ok ? drow0 + n0 + rloc : 0, dK)
-                 : F::row(hot, reinterpret_cast<const uint16_t*>(hot), 0, dK);
-        F::load(rw, ok ? dunit : 0, dst[j]);
+        const typename FD::Row rw =
+            live ? FD::row(a.down.base + ex * a.down.stride, ds, ok ? drow0 + n0 + rloc : 0, dK)
+                 : FD::row(hot, reinterpret_cast<const uint16_t*>(hot), 0, dK);
+        FD::load(rw, ok ? dunit : 0, dst[j]);
       }
     }
   };
@@ -853,7 +854,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
     return true;
   };
-  auto compute_dn = [&](int uu, const typename F::Raw(&src)[kDnSlot]) {
+  auto compute_dn = [&](int uu, const typename FD::Raw(&src)[kDnSlot]) {
     consume(src);
     const uint32_t mask = grp_mask(uu);
     if constexpr (DNK > 0) {
@@ -864,7 +865,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
       for (int ks = 0; ks < DNK; ++ks) {
         uint32_t e, q[4];
-        F::unpack(src[ks], (uint32_t)dblk[ks] & 3u, e, q);
+        FD::unpack(src[ks], (uint32_t)dblk[ks] & 3u, e, q);
         // Rows or blocks outside the matrix contribute zeros (E2M1 has no
         // NaN, and a unit scale keeps the products finite).
         A[ks] = v8i{(int)(dok[ks] ? q[0] : 0u), (int)(dok[ks] ? q[1] : 0u), (int)(dok[ks] ? q[2] : 0u),
@@ -930,7 +931,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
           const int v = lane + kWave * j;
           const int rloc = w * RPV + v / UPS;
           const bool ok = v < UD && rloc < RPWd && n0 + rloc < D;
-          float pr = ok ? F::dn_dot(src[j], dsh, hu) : 0.0f;
+          float pr = ok ? FD::dn_dot(src[j], dsh, hu) : 0.0f;
           pr = group_sum_dpp<UPS>(pr);
           if (ok && ub == 0) syp[s * RPWd + rloc] = pr;
         }
@@ -940,7 +941,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // Matrix-core down for prologue slots j0 .. j0 + kDnBatch - 1 in one
   // straight-line block (requires dn_full and groups of at most 4 tokens).
   // Slots past the last group compute on the zero operand and store nothing.
-  constexpr int kDnBatch = (Rings<F>::kDN - 1 + 1) / 2;
+  constexpr int kDnBatch = (Rings<FD>::kDN - 1 + 1) / 2;
   auto down_walk_batch = [&](auto j0c) {
     if constexpr (DNK > 0) {
       constexpr int j0 = decltype(j0c)::value;
@@ -965,7 +966,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
         for (int ks = 0; ks < DNK; ++ks) {
           uint32_t e, q[4];
-          F::unpack(dring[j][ks], (uint32_t)dblk[ks] & 3u, e, q);
+          FD::unpack(dring[j][ks], (uint32_t)dblk[ks] & 3u, e, q);
           A[b][ks] = v8i{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
           ea[b][ks] = (int)e;
           const uint4* bp = reinterpret_cast<const uint4*>(hb + (size_t)sl[b] * kHbSlot + ((ks * 4 + mg) * 4 + c) * 32);
@@ -1000,7 +1001,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // together.  A wave's first pass also requests the down prologue between
   // its first gate/up slots, so the gate/up data that the ring waits for
   // first is not queued behind down weights used only after the exchange.
-  static_assert(2 * Rings<F>::kGU >= Rings<F>::kDN - 1, "down prologue fits the first gate/up pass");
+  static_assert(2 * Rings<F>::kGU >= Rings<FD>::kDN - 1, "down prologue fits the first gate/up pass");
   {
     const int NR = max(0, min(RPW, FS - jx * RPW));  // rows of this workgroup
     const int NI = NR * U;
@@ -1131,15 +1132,15 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         const int i = i0 + q * g_step;
         if (valid[q]) {
           const int s = i / FS, f = i - (i / FS) * FS;
-          sh[(s * UPS + f / F::kUnitW) * kHB + f % F::kUnitW] = __uint_as_float(payload_of(v[q]));
+          sh[(s * UPS + f / FD::kUnitW) * kHB + f % FD::kUnitW] = __uint_as_float(payload_of(v[q]));
         }
       }
     }
     stamp(a, 12);
     if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints + 13] = (uint64_t)trace_rereads;
     __syncthreads();
-    if (F::kPrepH) {
-      for (int i = threadIdx.x; i < S * UPS; i += kW * kWave) F::prep_h(sh + i * kHB);
+    if (FD::kPrepH) {
+      for (int i = threadIdx.x; i < S * UPS; i += kW * kWave) FD::prep_h(sh + i * kHB);
       __syncthreads();
     }
   }
@@ -1239,40 +1240,40 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
 }
 
-template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM>
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD>
 hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK, NORM>), dim3(grid), dim3(kW * kWave), 0, s,
-                     a);
+  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK, NORM, FD>), dim3(grid), dim3(kW * kWave), 0,
+                     s, a);
   return hipGetLastError();
 }
 
 // DNK: k-steps of the matrix-core down projection (0: vector path).  NORM
 // (the kernel normalises the residual stream itself) exists for the
-// matrix-core path only.
-template <class F, int UPS, int DNK, bool NORM = false>
+// matrix-core path only.  FD: format of the down projection.
+template <class F, int UPS, int DNK, bool NORM = false, class FD = F>
 hipError_t launch_fused_f(const FusedArgs& a, int grid, int gu_units, int dn_units, hipStream_t s) {
   if constexpr (DNK > 0) {
-    return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, DNK, NORM>(a, grid, s)
-                            : launch_fused_t<F, 1, 1, UPS, DNK, NORM>(a, grid, s);
+    return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, DNK, NORM, FD>(a, grid, s)
+                            : launch_fused_t<F, 1, 1, UPS, DNK, NORM, FD>(a, grid, s);
   } else {
     static_assert(!NORM, "the in-kernel norm is built for the matrix-core path");
     if (gu_units > kWave) {
-      return dn_units > kWave ? launch_fused_t<F, 2, 2, UPS, 0, false>(a, grid, s)
-                              : launch_fused_t<F, 2, 1, UPS, 0, false>(a, grid, s);
+      return dn_units > kWave ? launch_fused_t<F, 2, 2, UPS, 0, false, FD>(a, grid, s)
+                              : launch_fused_t<F, 2, 1, UPS, 0, false, FD>(a, grid, s);
     }
-    return dn_units > kWave ? launch_fused_t<F, 1, 2, UPS, 0, false>(a, grid, s)
-                            : launch_fused_t<F, 1, 1, UPS, 0, false>(a, grid, s);
+    return dn_units > kWave ? launch_fused_t<F, 1, 2, UPS, 0, false, FD>(a, grid, s)
+                            : launch_fused_t<F, 1, 1, UPS, 0, false, FD>(a, grid, s);
   }
 }
 
-template <class F>
+template <class F, class FD = F>
 hipError_t launch_fused_ups(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s) {
   switch (ups) {
-    case 1: return launch_fused_f<F, 1, 0>(a, grid, gu_units, dn_units, s);
-    case 2: return launch_fused_f<F, 2, 0>(a, grid, gu_units, dn_units, s);
-    case 4: return launch_fused_f<F, 4, 0>(a, grid, gu_units, dn_units, s);
-    case 8: return launch_fused_f<F, 8, 0>(a, grid, gu_units, dn_units, s);
-    case 16: return launch_fused_f<F, 16, 0>(a, grid, gu_units, dn_units, s);
+    case 1: return launch_fused_f<F, 1, 0, false, FD>(a, grid, gu_units, dn_units, s);
+    case 2: return launch_fused_f<F, 2, 0, false, FD>(a, grid, gu_units, dn_units, s);
+    case 4: return launch_fused_f<F, 4, 0, false, FD>(a, grid, gu_units, dn_units, s);
+    case 8: return launch_fused_f<F, 8, 0, false, FD>(a, grid, gu_units, dn_units, s);
+    case 16: return launch_fused_f<F, 16, 0, false, FD>(a, grid, gu_units, dn_units, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1296,6 +1297,9 @@ hipError_t launch_mx_mfma(const FusedArgs& a, int grid, int gu_units, int ups, h
 hipError_t launch_mx_mfma_norm(const FusedArgs& a, int grid, int gu_units, int ups, hipStream_t s);
 hipError_t launch_q2k(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
 hipError_t launch_int4(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
+// gate/up in MXFP4 or INT4, down in Q2_K
+hipError_t launch_mx_q2k(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
+hipError_t launch_int4_q2k(const FusedArgs& a, int grid, int gu_units, int dn_units, int ups, hipStream_t s);
 
 }  // namespace fused
 }  // namespace moe

@@ -342,7 +342,8 @@ struct FusedShape {
   int gu_units, dn_units, ups;
 };
 int fused_grid_size();
-FusedShape fused_shape(int fmt, int B, int k, int D, int F, int grid, int nx, int down_layout);
+// fmt: gate/up format, dfmt: down format (enum moe_format).
+FusedShape fused_shape(int fmt, int dfmt, int B, int k, int D, int F, int grid, int nx, int down_layout);
 // XCD count of the current device, measured once per device (the probe
 // synchronises `s`; scratch needs grid uint32).  xcd_count(): 0 not measured
 // yet, -1 placement unsuitable for the single-launch layer, else the count.
@@ -351,7 +352,7 @@ int xcd_count();
 // x: bf16 activations [B][D]; or, with hn set (x unused), the residual
 // stream fp32 [1][D] of one token that the kernel RMS-normalises itself
 // (B = 1, D <= 4096, D % 8 == 0, matrix-core layout; hn must not alias y).
-hipError_t launch_fused_layer(int fmt, const float* router_w, const uint16_t* x, const float* hn, double eps,
+hipError_t launch_fused_layer(int fmt, int dfmt, const float* router_w, const uint16_t* x, const float* hn, double eps,
                               const WeightRef& gate, const WeightRef& up, const WeightRef& down, int E, int D, int Fd,
                               int k, int B, uint8_t* ws, const WsLayout& L, float* y, const float* residual,
                               int32_t* idx_out, float* gw_out, uint64_t* trace, hipStream_t s);

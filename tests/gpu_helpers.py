@@ -60,78 +60,78 @@ class Layer:
     fmt "int4g32": MXFP4 weights filled on the GPU, then converted by
     quantize_fp4_to_int4g32 (the conversion under test elsewhere); the oracle
     side converts its own twin bytes with oracle.quantize_fp4_to_int4g32.
+    ``down_fmt``: the down projection's format when it differs (per-family
+    precision); ``fmt`` then covers gate and up.
     """
 
     def __init__(self, fmt: str, seed: int, layer: int, E: int, D: int, F: int, top_k: int = 6,
-                 down_layout: str = "rows"):
+                 down_layout: str = "rows", down_fmt: str | None = None):
         self.fmt, self.seed, self.layer = fmt, seed, layer
+        self.down_fmt = down_fmt or fmt
         self.E, self.D, self.F, self.k = E, D, F, top_k
         self.down_layout = down_layout
         self.router = synth.router_weights(seed, layer, E, D)
         self.router_dev = dev(self.router)
-        src = "mxfp4" if fmt == "int4g32" else fmt
-        self.src = src
-        self.bytes = {}
+        self.pfmt = {synth.PROJ_GATE: fmt, synth.PROJ_UP: fmt, synth.PROJ_DOWN: self.down_fmt}
+        self.shape = {synth.PROJ_GATE: (F, D), synth.PROJ_UP: (F, D), synth.PROJ_DOWN: (D, F)}
         stream = torch.cuda.current_stream().cuda_stream
-        for proj, (n, kk) in ((synth.PROJ_GATE, (F, D)), (synth.PROJ_UP, (F, D)), (synth.PROJ_DOWN, (D, F))):
+        self.w = {}  # projection -> (base, stride, scale base or None, scale stride)
+        for proj in (synth.PROJ_GATE, synth.PROJ_UP, synth.PROJ_DOWN):
+            pf = self.pfmt[proj]
+            src = "mxfp4" if pf == "int4g32" else pf
+            n, kk = self.shape[proj]
             per = matrix_bytes(src, n, kk)
             stride = (per + 255) // 256 * 256
             buf = torch.empty(E * stride, dtype=torch.uint8, device="cuda")
             bw, bb = BLOCK[src]
             for e in range(E):
-                synth.gpu_fill(src, buf.data_ptr() + e * stride, seed, layer, e, 1, proj,
-                               n * (kk // bw), stream)
-            self.bytes[proj] = (buf, stride)
-        if fmt == "int4g32":
-            self.q = {}
-            for proj, (n, kk) in ((synth.PROJ_GATE, (F, D)), (synth.PROJ_UP, (F, D)), (synth.PROJ_DOWN, (D, F))):
-                buf, stride = self.bytes[proj]
+                synth.gpu_fill(src, buf.data_ptr() + e * stride, seed, layer, e, 1, proj, n * (kk // bw), stream)
+            tiled = proj == synth.PROJ_DOWN and down_layout != "rows"
+            if pf == "int4g32":
                 qstride = n * kk // 2
                 sstride = (n * (kk // 32) * 2 + 255) // 256 * 256
                 q = torch.empty(E * qstride, dtype=torch.uint8, device="cuda")
-                s = torch.empty(E * sstride, dtype=torch.uint8, device="cuda")
+                sc = torch.empty(E * sstride, dtype=torch.uint8, device="cuda")
                 for e in range(E):
                     moe.quantize_fp4_to_int4g32(buf.data_ptr() + e * stride, n, kk, q.data_ptr() + e * qstride,
-                                                s.data_ptr() + e * sstride)
-                self.q[proj] = (q, qstride, s, sstride)
-            del self.bytes
-            if down_layout == "tile256":  # same buffers' shapes, blocks permuted per expert
-                q, qstride, sc, sstride = self.q[synth.PROJ_DOWN]
-                qt, st = torch.empty_like(q), torch.empty_like(sc)
-                for e in range(E):
-                    moe.moe_tile_weights("int4g32", q.data_ptr() + e * qstride, D, F, qt.data_ptr() + e * qstride,
-                                         src_scale=sc.data_ptr() + e * sstride, dst_scale=st.data_ptr() + e * sstride)
-                self.q[synth.PROJ_DOWN] = (qt, qstride, st, sstride)
-            torch.cuda.synchronize()
-            self.desc = moe.make_layer_desc(
-                fmt, self.router_dev, self.q[0][0], self.q[1][0], self.q[2][0], E, D, F, top_k,
-                self.q[0][1], self.q[1][1], self.q[2][1], self.q[0][2], self.q[1][2], self.q[2][2],
-                self.q[0][3], self.q[1][3], self.q[2][3], down_layout=down_layout)
-        else:
-            if down_layout in ("tile256", "mfma16"):
-                buf, stride = self.bytes[synth.PROJ_DOWN]
-                bt = torch.empty_like(buf)
-                for e in range(E):
-                    if down_layout == "tile256":
-                        moe.moe_tile_weights(fmt, buf.data_ptr() + e * stride, D, F, bt.data_ptr() + e * stride)
-                    else:
-                        moe.moe_tile_weights_mfma16(buf.data_ptr() + e * stride, D, F, bt.data_ptr() + e * stride)
-                self.bytes[synth.PROJ_DOWN] = (bt, stride)
-                torch.cuda.synchronize()
-            self.desc = moe.make_layer_desc(
-                fmt, self.router_dev, self.bytes[0][0], self.bytes[1][0], self.bytes[2][0], E, D, F, top_k,
-                self.bytes[0][1], self.bytes[1][1], self.bytes[2][1], down_layout=down_layout)
+                                                sc.data_ptr() + e * sstride)
+                del buf
+                if tiled:  # same buffers' shapes, blocks permuted per expert
+                    qt, st = torch.empty_like(q), torch.empty_like(sc)
+                    for e in range(E):
+                        moe.moe_tile_weights("int4g32", q.data_ptr() + e * qstride, n, kk,
+                                             qt.data_ptr() + e * qstride, src_scale=sc.data_ptr() + e * sstride,
+                                             dst_scale=st.data_ptr() + e * sstride)
+                    q, sc = qt, st
+                self.w[proj] = (q, qstride, sc, sstride)
+            else:
+                if tiled:
+                    bt = torch.empty_like(buf)
+                    for e in range(E):
+                        if down_layout == "tile256":
+                            moe.moe_tile_weights(pf, buf.data_ptr() + e * stride, n, kk, bt.data_ptr() + e * stride)
+                        else:
+                            moe.moe_tile_weights_mfma16(buf.data_ptr() + e * stride, n, kk,
+                                                        bt.data_ptr() + e * stride)
+                    buf = bt
+                self.w[proj] = (buf, stride, None, 0)
+        torch.cuda.synchronize()
+        g, u, d = (self.w[p] for p in (synth.PROJ_GATE, synth.PROJ_UP, synth.PROJ_DOWN))
+        self.desc = moe.make_layer_desc(
+            fmt, self.router_dev, g[0], u[0], d[0], E, D, F, top_k, g[1], u[1], d[1], g[2], u[2], d[2],
+            g[3], u[3], d[3], down_layout=down_layout, down_format=self.down_fmt)
         self._cache = {}
 
     # -- oracle side: regenerate expert e's bytes with the host twin
     def expert_host(self, e: int):
         if e in self._cache:
             return self._cache[e]
-        D, F = self.D, self.F
         mats = []
-        for proj, (n, kk) in ((synth.PROJ_GATE, (F, D)), (synth.PROJ_UP, (F, D)), (synth.PROJ_DOWN, (D, F))):
-            b = synth.expert_tensor(self.src, self.seed, self.layer, e, proj, n, kk)
-            if self.fmt == "int4g32":
+        for proj in (synth.PROJ_GATE, synth.PROJ_UP, synth.PROJ_DOWN):
+            pf = self.pfmt[proj]
+            n, kk = self.shape[proj]
+            b = synth.expert_tensor("mxfp4" if pf == "int4g32" else pf, self.seed, self.layer, e, proj, n, kk)
+            if pf == "int4g32":
                 b = oracle.quantize_fp4_to_int4g32(b, n, kk)
             mats.append(b)
         self._cache[e] = tuple(mats)
@@ -158,4 +158,4 @@ class Layer:
         return host(y), host(idx), host(gw)
 
     def oracle(self, x_bf16: np.ndarray):
-        return oracle.layer_decode(self.fmt, self.expert_host, self.router, x_bf16, self.k, self.F)
+        return oracle.layer_decode((self.fmt, self.down_fmt), self.expert_host, self.router, x_bf16, self.k, self.F)

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert moe.moe_abi_version() == moe.ABI_VERSION == 3
+    assert moe.moe_abi_version() == moe.ABI_VERSION == 4
     for st in range(7):
         assert moe.moe_status_string(st)
     assert moe.moe_status_string(0) == "ok"
@@ -102,6 +102,27 @@ def test_layer_and_route_validation_on_host(L):
     assert L.quantize_fp4_to_int4g32(FAKE, 8, 48, FAKE, FAKE, None) == 2
     assert L.quantize_fp4_to_int4g32(FAKE, 8, 64, FAKE + 4, FAKE, None) == 6
     assert L.moe_validate_mxfp4(FAKE, -1, FAKE, None) == 1
+
+
+def test_mixed_format_validation_on_host(L):
+    """Per-family precision: gate/up in one format, down in another."""
+    d = moe.make_layer_desc("mxfp4", FAKE, FAKE, FAKE, FAKE, 256, 4096, 2048, 6, 4456704, 4456704, 2752512,
+                            down_format="q2k")
+    assert d.down_format == 2
+    assert moe.make_layer_desc("q2k", FAKE, FAKE, FAKE, FAKE, 8, 256, 256, 2, 256, 256, 256,
+                               down_format="q2k").down_format == 0        # same format: the zero default
+    ws_ok = 1 << 30
+    run = lambda: L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, ws_ok, None, None, None)
+    d.down_format = 4                                   # not a format
+    assert run() == 1
+    d.down_format, d.d_ff = 2, 2080                     # Q2_K down: d_ff % 256 (and MXFP4's 32 holds)
+    assert run() == 2
+    d.d_ff, d.down_layout = 2048, 2                     # the matrix-core layout needs an MXFP4 down
+    assert run() == 1
+    d.down_layout, d.down_stride = 0, 2752514           # the down format's alignment rules
+    assert run() == 6
+    d.down_stride, d.down_format = 2752512, 3           # INT4 down needs its scales
+    assert run() == 1
 
 
 def test_layout_validation_on_host(L):
