@@ -103,7 +103,8 @@ def build_layers(n_layers: int, seed: int, down_layout: str = "mfma16"):
 Q2K_MAT = F * (D // 256) * 84        # 2,752,512 bytes per projection (gate/up [F][D] and down [D][F])
 I4_Q = F * D // 2                    # INT4 codes per projection
 I4_S = F * (D // 32) * 2             # bfloat16 scales per projection
-EXPERT_BYTES = {"mxfp4": 3 * MX_MAT, "q2k": 3 * Q2K_MAT, "int4g32": 3 * (I4_Q + I4_S)}
+EXPERT_BYTES = {"mxfp4": 3 * MX_MAT, "q2k": 3 * Q2K_MAT, "int4g32": 3 * (I4_Q + I4_S),
+                "mxfp4+q2k": 2 * MX_MAT + Q2K_MAT}
 
 
 def build_format_layers(fmt: str, n_layers: int, seed: int):
@@ -118,7 +119,24 @@ def build_format_layers(fmt: str, n_layers: int, seed: int):
         return build_layers(n_layers, seed, "mfma16")
     stream = torch.cuda.current_stream().cuda_stream
     layers = []
-    if fmt == "q2k":
+    if fmt == "mxfp4+q2k":  # per-family precision: MXFP4 gate/up, tiled Q2_K down
+        tmp = torch.empty(E * Q2K_MAT, dtype=torch.uint8, device="cuda")
+        for l in range(n_layers):
+            mats = []
+            for proj in (synth.PROJ_GATE, synth.PROJ_UP):
+                buf = torch.empty(E * MX_MAT, dtype=torch.uint8, device="cuda")
+                synth.gpu_fill("mxfp4", buf.data_ptr(), seed, l, 0, E, proj, F * D // 32, stream)
+                mats.append(buf)
+            buf = torch.empty(E * Q2K_MAT, dtype=torch.uint8, device="cuda")
+            synth.gpu_fill("q2k", tmp.data_ptr(), seed, l, 0, E, synth.PROJ_DOWN, F * D // 256, stream)
+            for e in range(E):
+                moe.moe_tile_weights("q2k", tmp.data_ptr() + e * Q2K_MAT, D, F, buf.data_ptr() + e * Q2K_MAT)
+            mats.append(buf)
+            router = torch.from_numpy(synth.router_weights(seed, l, E, D)).to("cuda")
+            desc = moe.make_layer_desc("mxfp4", router, mats[0], mats[1], mats[2], E, D, F, TOPK,
+                                       MX_MAT, MX_MAT, Q2K_MAT, down_layout="tile256", down_format="q2k")
+            layers.append((desc, mats, router))
+    elif fmt == "q2k":
         tmp = torch.empty(E * Q2K_MAT, dtype=torch.uint8, device="cuda")
         for l in range(n_layers):
             mats = []
@@ -188,18 +206,18 @@ def format_leg(fmt: str, n_layers: int, seed: int, steps: int, warmup: int, ws):
     return out
 
 
-def stack_leg(n_layers: int, seed: int, steps: int, warmup: int, mean_u8: float):
-    """The residual stream through n_layers resident MXFP4 layers (moe_stack_decode)."""
+def stack_leg(n_layers: int, seed: int, steps: int, warmup: int, mean_u8: float, fmt: str = "mxfp4"):
+    """The residual stream through n_layers resident layers (moe_stack_decode)."""
     import torch
 
     import quantized_moe_decode_route_amd as moe
     import synth
-    log(f"stack: building {n_layers} MXFP4 layers ({n_layers * 3 * E * MX_MAT / 1e9:.0f} GB resident) ...")
-    layers = build_layers(n_layers, seed, "mfma16")
+    log(f"stack: building {n_layers} {fmt} layers ({n_layers * E * EXPERT_BYTES[fmt] / 1e9:.0f} GB resident) ...")
+    layers = build_format_layers(fmt, n_layers, seed)
     descs = [l[0] for l in layers]
     ws = torch.empty(moe.moe_stack_workspace_bytes(8, D, F, E, TOPK), dtype=torch.uint8, device="cuda")
     moe.moe_workspace_init(ws)
-    out = {"layers": n_layers, "resident_bytes": n_layers * (3 * E * MX_MAT + ROUTER)}
+    out = {"layers": n_layers, "format": fmt, "resident_bytes": n_layers * (E * EXPERT_BYTES[fmt] + ROUTER)}
     for B in (1, 8):
         hs = [torch.from_numpy(synth.token_f32(70000 + 31 * B + i, B, D)).to("cuda") for i in range(warmup + steps)]
         hout = torch.empty((B, D), dtype=torch.float32, device="cuda")
@@ -214,7 +232,7 @@ def stack_leg(n_layers: int, seed: int, steps: int, warmup: int, mean_u8: float)
         torch.cuda.synchronize()
         ms = start.elapsed_time(end) / steps
         u = TOPK if B == 1 else mean_u8
-        nbytes = n_layers * (u * EXPERT_BYTES["mxfp4"] + ROUTER)
+        nbytes = n_layers * (u * EXPERT_BYTES[fmt] + ROUTER)
         out[f"b{B}"] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * 1e3 / ms, 1),
                         "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
                         "bytes_per_step": round(nbytes),
@@ -439,8 +457,11 @@ def main():
         del layers
         torch.cuda.empty_cache()
         ext_steps, ext_warm = max(args.steps // 2, 10), max(args.warmup // 2, 5)
-        result["formats"] = {f: format_leg(f, 4, args.seed + 7, ext_steps, ext_warm, ws) for f in ("q2k", "int4g32")}
+        result["formats"] = {f: format_leg(f, 4, args.seed + 7, ext_steps, ext_warm, ws)
+                             for f in ("q2k", "int4g32", "mxfp4+q2k")}
         result["stack"] = stack_leg(args.stack_layers, args.seed + 11, 10, 2, U8)
+        result["stack_q2k"] = stack_leg(args.stack_layers, args.seed + 13, 10, 2,
+                                        result["formats"]["q2k"]["b8"]["mean_unique_experts"], fmt="q2k")
         log("matvec ...")
         result["gemv_mxfp4_2048x4096"] = gemv_leg(args.steps, args.warmup)
     if not args.no_cpu_baseline:
