@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 enum moe_status {
   MOE_OK = 0,
@@ -171,6 +171,20 @@ typedef struct moe_layer_desc {
    * formats' block lengths).  A zeroed field keeps every projection in
    * `format`. */
   int down_format;
+  /* Hash-routed layer ("cabbage v4x quant surgery": the first 3 of the 43
+   * layers route by a fixed hash of the token id, through the tid2eid table,
+   * instead of by the learned router).  NULL: learned routing.  Otherwise
+   * int32 [vocab][top_k] device table whose row for token id t lists that
+   * token's experts in rank order; the gate weights are the softmax over the
+   * router logits of those experts (the reading used here: the pages keep a
+   * gate matrix for these layers but do not give their weighting), and such a
+   * layer is called through the *_ids entry points with the tokens' ids.  A
+   * row that is out of range, holds an expert outside [0, n_experts) or
+   * repeats one, or an id outside [0, vocab), routes that token to experts
+   * 0..top_k-1 instead and sets the workspace's bad-input flag
+   * (moe_workspace_flags). */
+  const int32_t* tid2eid;
+  int vocab;
 } moe_layer_desc;
 enum moe_down_format { MOE_DOWN_SAME = 0, MOE_DOWN_MXFP4 = 1, MOE_DOWN_Q2K = 2, MOE_DOWN_INT4G32 = 3 };
 
@@ -183,6 +197,16 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * receive the routing if not NULL. */
 int moe_layer_decode(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
                      size_t ws_bytes, int32_t* idx_out, float* gw_out, void* stream);
+/* The same layer with the tokens' ids (device int32 [B]), required by a
+ * hash-routed layer (tid2eid set) and ignored otherwise (may be NULL then).
+ * moe_layer_decode on a hash-routed layer returns MOE_ERR_ARG. */
+int moe_layer_decode_ids(const moe_layer_desc* L, const int32_t* token_ids, const uint16_t* x_bf16, int B,
+                         float* y, void* ws, size_t ws_bytes, int32_t* idx_out, float* gw_out, void* stream);
+/* Sticky error flags of a layer or stack workspace, copied to the host
+ * (synchronises `stream`): bit 0 a bounded wait gave up, bit 1 a hash-routed
+ * layer met an invalid token id or table row.  They stay set until
+ * moe_workspace_init. */
+int moe_workspace_flags(const void* ws, size_t ws_bytes, uint32_t* flags, void* stream);
 /* Same, recording two hipEvent_t (passed as void*) on `stream` right before
  * and right after the layer's kernels, for timing.  Either may be NULL. */
 int moe_layer_decode_profiled(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
@@ -220,6 +244,11 @@ int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int
 size_t moe_stack_workspace_bytes(int B, int D, int F, int E, int top_k);
 int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* h_in, int B,
                      float* h_out, double eps, void* ws, size_t ws_bytes, void* stream);
+/* The stack with the tokens' ids (device int32 [B]) for its hash-routed
+ * layers; moe_stack_decode returns MOE_ERR_ARG if any layer is hash-routed. */
+int moe_stack_decode_ids(const moe_layer_desc* layers, int n_layers, const int32_t* token_ids,
+                         const float* h_in, int B, float* h_out, double eps, void* ws, size_t ws_bytes,
+                         void* stream);
 /* The norm step alone: x_out bfloat16 bits [B][D] from h fp32 [B][D]. */
 int moe_rmsnorm_bf16(const float* h, int B, int D, double eps, uint16_t* x_out, void* stream);
 

@@ -93,6 +93,9 @@ def lib():
                                            ctypes.c_int]
         L.oracle_topk_softmax.restype = ctypes.c_int
         L.oracle_topk_softmax.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _dp]
+        L.oracle_hash_route.restype = ctypes.c_int
+        L.oracle_hash_route.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, ctypes.c_int, _i32p,
+                                        _i32p, _dp, ctypes.POINTER(ctypes.c_int)]
         L.oracle_silu_mul.restype = None
         L.oracle_silu_mul.argtypes = [_dp, _dp, ctypes.c_int64, _dp]
         L.oracle_rmsnorm_bf16.restype = None
@@ -250,6 +253,30 @@ def route_topk(wr: np.ndarray, x_bf16: np.ndarray, k: int = 6):
     return idx, g, logits
 
 
+def hash_route(logits: np.ndarray, k: int, table: np.ndarray, ids: np.ndarray):
+    """Hash-routed selection from given logits [B, E]: ``table`` int32 [vocab, k],
+    ``ids`` int32 [B].  Returns (idx int32 [B, k], g fp64 [B, k], number of
+    tokens with an invalid id or row, which use experts 0..k-1)."""
+    l = np.ascontiguousarray(logits, dtype=np.float64)
+    B, E = l.shape
+    tb = np.ascontiguousarray(table, dtype=np.int32)
+    iv = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+    idx = np.empty((B, k), dtype=np.int32)
+    g = np.empty((B, k), dtype=np.float64)
+    nb = ctypes.c_int(0)
+    _check(lib().oracle_hash_route(l.reshape(-1), E, B, k, tb.reshape(-1), tb.shape[0], iv, idx.reshape(-1),
+                                   g.reshape(-1), ctypes.byref(nb)), "hash_route")
+    return idx, g, nb.value
+
+
+def route_hashed(wr: np.ndarray, x_bf16: np.ndarray, table: np.ndarray, ids: np.ndarray, k: int = 6):
+    """Router logits as in route_topk, experts from the tid2eid table."""
+    x = bf16_rows_to_f64(x_bf16)
+    logits = router_logits(wr, x)
+    idx, g, _ = hash_route(logits, k, table, ids)
+    return idx, g, logits
+
+
 def silu_mul(gate: np.ndarray, up: np.ndarray) -> np.ndarray:
     g = np.ascontiguousarray(gate, dtype=np.float64).reshape(-1)
     u = np.ascontiguousarray(up, dtype=np.float64).reshape(-1)
@@ -283,8 +310,9 @@ def expert_ffn(fmt, gate, up, down, x: np.ndarray, d_model: int, d_ff: int) -> n
 
 
 def layer_decode(fmt, get_expert, wr: np.ndarray, x_bf16: np.ndarray, top_k: int = 6,
-                 d_ff: int | None = None):
-    """One MoE layer for B tokens (``fmt`` as in ``expert_ffn``).
+                 d_ff: int | None = None, hashed=None):
+    """One MoE layer for B tokens (``fmt`` as in ``expert_ffn``); ``hashed``:
+    (tid2eid table, token ids) for a hash-routed layer.
 
     ``get_expert(e)`` returns ``(gate, up, down)`` weights of expert ``e``.
     Returns ``(y fp64 [B, D], idx int32 [B, k], g fp64 [B, k])``.
@@ -292,7 +320,10 @@ def layer_decode(fmt, get_expert, wr: np.ndarray, x_bf16: np.ndarray, top_k: int
     E, D = wr.shape
     xb = np.asarray(x_bf16, dtype=np.uint16).reshape(-1, D)
     x = bf16_rows_to_f64(xb)
-    idx, g, _ = route_topk(wr, xb, top_k)
+    if hashed is None:
+        idx, g, _ = route_topk(wr, xb, top_k)
+    else:
+        idx, g, _ = route_hashed(wr, xb, hashed[0], hashed[1], top_k)
     B = x.shape[0]
     y = np.zeros((B, D), dtype=np.float64)
     cache = {}

@@ -352,6 +352,44 @@ int oracle_topk_softmax(const double* logits, int E, int B, int k, int32_t* idx,
   return ORACLE_OK;
 }
 
+/* Hash-routed layer ("cabbage v4x quant surgery": the first 3 of the 43
+ * layers map each token to experts by a fixed hash of its id, the tid2eid
+ * table, independent of the weights): token b uses experts
+ * table[ids[b]][0..k-1] in that order.  Its gate weights are the softmax over
+ * those experts' router logits (fp64, shifted by the largest of them, summed
+ * in table order) -- a reading: the pages keep a gate matrix for these layers
+ * without saying how it weighs the experts.  An id outside [0, vocab), or a
+ * row with an expert outside [0, E) or a repeated one, routes the token to
+ * experts 0..k-1; *n_bad counts such tokens. */
+int oracle_hash_route(const double* logits, int E, int B, int k, const int32_t* table, int vocab,
+                      const int32_t* ids, int32_t* idx, double* g, int* n_bad) {
+  if (!logits || !table || !ids || !idx || !g || !n_bad || k <= 0 || k > E || B < 0 || vocab <= 0)
+    return ORACLE_ERR_ARG;
+  *n_bad = 0;
+  for (int b = 0; b < B; ++b) {
+    const double* l = logits + (int64_t)b * E;
+    int ok = ids[b] >= 0 && ids[b] < vocab;
+    const int32_t* row = table + (int64_t)(ok ? ids[b] : 0) * k;
+    for (int r = 0; r < k && ok; ++r) {
+      if (row[r] < 0 || row[r] >= E) ok = 0;
+      for (int q = 0; q < r && ok; ++q)
+        if (row[q] == row[r]) ok = 0;
+    }
+    if (!ok) ++*n_bad;
+    for (int r = 0; r < k; ++r) idx[b * k + r] = ok ? row[r] : r;
+    double m = l[idx[b * k]];
+    for (int r = 1; r < k; ++r)
+      if (l[idx[b * k + r]] > m) m = l[idx[b * k + r]];
+    double sum = 0.0;
+    for (int r = 0; r < k; ++r) {
+      g[b * k + r] = exp(l[idx[b * k + r]] - m);
+      sum += g[b * k + r];
+    }
+    for (int r = 0; r < k; ++r) g[b * k + r] /= sum;
+  }
+  return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------ expert FFN pieces */
 
 /* SiLU(z) = z * sigmoid(z) = z / (1 + e^-z).  Not defined on the pages; this

@@ -20,7 +20,7 @@ FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2k": MOE_FMT_Q2K, "int4g32": MOE_FMT_INT4G3
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE256, MOE_LAYOUT_MFMA16 = 0, 1, 2
 LAYOUTS = {"rows": MOE_LAYOUT_ROWS, "tile256": MOE_LAYOUT_TILE256, "mfma16": MOE_LAYOUT_MFMA16}
 # MOE_ABI_VERSION of include/moe_decode.h that this binding is written for
-ABI_VERSION = 4
+ABI_VERSION = 5
 MOE_MAX_TOKENS = 8
 MOE_MAX_TOPK = 8
 
@@ -28,9 +28,9 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "moe_last_hip_error", "moe_device_check",
     "moe_expert_gemv_mxfp4", "moe_expert_gemv_q2k", "moe_expert_gemv_int4g32",
     "moe_route_workspace_bytes", "moe_route_topk",
-    "moe_layer_workspace_bytes", "moe_workspace_init", "moe_layer_decode", "moe_layer_decode_profiled",
-    "moe_layer_decode_traced",
-    "moe_stack_workspace_bytes", "moe_stack_decode", "moe_rmsnorm_bf16",
+    "moe_layer_workspace_bytes", "moe_workspace_init", "moe_layer_decode", "moe_layer_decode_ids",
+    "moe_workspace_flags", "moe_layer_decode_profiled", "moe_layer_decode_traced",
+    "moe_stack_workspace_bytes", "moe_stack_decode", "moe_stack_decode_ids", "moe_rmsnorm_bf16",
     "quantize_fp4_to_int4g32", "moe_validate_mxfp4", "moe_tile_weights", "moe_tile_weights_mfma16",
 )
 
@@ -55,6 +55,7 @@ class moe_layer_desc(ctypes.Structure):
         ("gate_scale_stride", ctypes.c_int64), ("up_scale_stride", ctypes.c_int64),
         ("down_scale_stride", ctypes.c_int64),
         ("down_layout", ctypes.c_int), ("down_format", ctypes.c_int),
+        ("tid2eid", ctypes.c_void_p), ("vocab", ctypes.c_int),
     ]
 
 
@@ -82,12 +83,17 @@ def lib() -> ctypes.CDLL:
             "moe_layer_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
             "moe_workspace_init": (_i, [_vp, _sz, _vp]),
             "moe_layer_decode": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _sz, _vp, _vp, _vp]),
+            "moe_layer_decode_ids": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _vp, _i, _vp, _vp, _sz, _vp, _vp,
+                                          _vp]),
+            "moe_workspace_flags": (_i, [_vp, _sz, ctypes.POINTER(ctypes.c_uint32), _vp]),
             "moe_layer_decode_profiled": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _sz, _vp, _vp,
                                                ctypes.POINTER(_vp), _vp]),
             "moe_layer_decode_traced": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _sz, _vp,
                                              ctypes.POINTER(_i), _vp]),
             "moe_stack_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
             "moe_stack_decode": (_i, [ctypes.POINTER(moe_layer_desc), _i, _vp, _i, _vp, _d, _vp, _sz, _vp]),
+            "moe_stack_decode_ids": (_i, [ctypes.POINTER(moe_layer_desc), _i, _vp, _vp, _i, _vp, _d, _vp, _sz,
+                                          _vp]),
             "moe_rmsnorm_bf16": (_i, [_vp, _i, _i, _d, _vp, _vp]),
             "quantize_fp4_to_int4g32": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
             "moe_validate_mxfp4": (_i, [_vp, _i64, _vp, _vp]),
@@ -183,11 +189,13 @@ def make_layer_desc(fmt: str, router_w, gate, up, down, n_experts: int, d_model:
                     gate_stride: int, up_stride: int, down_stride: int, gate_scale=None, up_scale=None,
                     down_scale=None, gate_scale_stride: int = 0, up_scale_stride: int = 0,
                     down_scale_stride: int = 0, down_layout: str = "rows",
-                    down_format: str | None = None) -> moe_layer_desc:
+                    down_format: str | None = None, tid2eid=None, vocab: int = 0) -> moe_layer_desc:
     """Fill the C descriptor; tensors (or raw device addresses) must outlive its use.
     ``down_layout``: "rows" (as published), "tile256" (see moe_tile_weights) or
     "mfma16" (MXFP4 only, see moe_tile_weights_mfma16).  ``down_format``: the
-    down projection's format when it differs from ``fmt`` (gate and up)."""
+    down projection's format when it differs from ``fmt`` (gate and up).  ``tid2eid``: int32
+    [vocab][top_k] table of a hash-routed layer (call it through the *_ids
+    entry points)."""
     d = moe_layer_desc()
     d.format = FORMATS[fmt]
     d.n_experts, d.d_model, d.d_ff, d.top_k = n_experts, d_model, d_ff, top_k
@@ -198,6 +206,7 @@ def make_layer_desc(fmt: str, router_w, gate, up, down, n_experts: int, d_model:
     d.gate_scale_stride, d.up_scale_stride, d.down_scale_stride = gate_scale_stride, up_scale_stride, down_scale_stride
     d.down_layout = LAYOUTS[down_layout]
     d.down_format = 0 if down_format is None or down_format == fmt else 1 + FORMATS[down_format]
+    d.tid2eid, d.vocab = _ptr(tid2eid), vocab
     return d
 
 
@@ -206,6 +215,24 @@ def moe_layer_decode(desc: moe_layer_desc, x_bf16, y, ws, idx_out=None, gw_out=N
     _check("moe_layer_decode",
            lib().moe_layer_decode(ctypes.byref(desc), _ptr(x_bf16), B, _ptr(y), _ptr(ws),
                                   ws.numel() * ws.element_size(), _ptr(idx_out), _ptr(gw_out), _stream(stream)))
+
+
+def moe_layer_decode_ids(desc: moe_layer_desc, token_ids, x_bf16, y, ws, idx_out=None, gw_out=None,
+                         stream=None) -> None:
+    """``token_ids``: device int32 [B] (required by a hash-routed layer)."""
+    B = x_bf16.shape[0]
+    _check("moe_layer_decode_ids",
+           lib().moe_layer_decode_ids(ctypes.byref(desc), _ptr(token_ids), _ptr(x_bf16), B, _ptr(y), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _ptr(idx_out), _ptr(gw_out),
+                                      _stream(stream)))
+
+
+def moe_workspace_flags(ws, stream=None) -> int:
+    """Bit 0: a bounded wait gave up; bit 1: a hash-routed layer met an invalid id or table row."""
+    f = ctypes.c_uint32(0)
+    _check("moe_workspace_flags",
+           lib().moe_workspace_flags(_ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(f), _stream(stream)))
+    return f.value
 
 
 def moe_layer_decode_profiled(desc: moe_layer_desc, x_bf16, y, ws, events, idx_out=None, gw_out=None,
@@ -253,6 +280,14 @@ def moe_stack_decode(descs, h_in, h_out, ws, eps: float = 1e-6, stream=None) -> 
     _check("moe_stack_decode",
            lib().moe_stack_decode(arr, len(descs), _ptr(h_in), B, _ptr(h_out), eps, _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_stack_decode_ids(descs, token_ids, h_in, h_out, ws, eps: float = 1e-6, stream=None) -> None:
+    arr = (moe_layer_desc * len(descs))(*descs)
+    B = h_in.shape[0]
+    _check("moe_stack_decode_ids",
+           lib().moe_stack_decode_ids(arr, len(descs), _ptr(token_ids), _ptr(h_in), B, _ptr(h_out), eps, _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_rmsnorm_bf16(h, x_out, eps: float = 1e-6, stream=None) -> None:

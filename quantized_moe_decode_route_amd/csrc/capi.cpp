@@ -82,6 +82,17 @@ int check_layer(const moe_layer_desc* L, int B) {
     if (!L->down_scale) return MOE_ERR_ARG;
     if (!aligned(L->down_scale, 2) || L->down_scale_stride % 2) return MOE_ERR_ALIGN;
   }
+  if (L->tid2eid) {
+    if (L->vocab < 1) return MOE_ERR_ARG;
+    if (!aligned(L->tid2eid, 4)) return MOE_ERR_ALIGN;
+  }
+  return MOE_OK;
+}
+
+// A hash-routed layer needs the tokens' ids.
+int check_ids(const moe_layer_desc* L, const int32_t* token_ids) {
+  if (L->tid2eid && !token_ids) return MOE_ERR_ARG;
+  if (token_ids && !aligned(token_ids, 4)) return MOE_ERR_ALIGN;
   return MOE_OK;
 }
 
@@ -100,7 +111,9 @@ WeightRef wref(const void* base, int64_t stride, const uint16_t* scale, int64_t 
 // otherwise the norm kernel writes them to xbuf first.
 int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, const float* residual, void* ws,
                int32_t* idx_out, float* gw_out, void* const* events, hipStream_t s, uint64_t* trace = nullptr,
-               const float* hn = nullptr, double eps = 0.0, uint16_t* xbuf = nullptr) {
+               const float* hn = nullptr, double eps = 0.0, uint16_t* xbuf = nullptr,
+               const int32_t* token_ids = nullptr) {
+  const HashRoute hr{L->tid2eid, token_ids, L->vocab};
   const int D = L->d_model, F = L->d_ff, E = L->n_experts, k = L->top_k;
   const WsLayout W = layer_ws_layout(B, D, F, E, k);
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -129,10 +142,10 @@ int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
   }
   if (fused) {
     e = launch_fused_layer(L->format, fd, L->router_w, x_bf16, hn, eps, g, u, d, E, D, F, k, B, w, W, y, residual,
-                           idx_out, gw_out, trace, s);
+                           idx_out, gw_out, trace, s, hr);
     if (e != hipSuccess) return hip_status(e);
   } else {
-    if ((e = launch_route(L->router_w, E, D, x_bf16, B, k, w, W, idx_out, gw_out, nullptr, s)) != hipSuccess)
+    if ((e = launch_route(L->router_w, E, D, x_bf16, B, k, w, W, idx_out, gw_out, nullptr, s, hr)) != hipSuccess)
       return hip_status(e);
     if ((e = launch_gate_up(L->format, g, u, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
     if ((e = launch_down(fd, d, D, F, B, k, w, W, s)) != hipSuccess) return hip_status(e);
@@ -149,6 +162,19 @@ int check_ws(void* ws, size_t have, size_t need) {
   return MOE_OK;
 }
 
+int layer_entry(const moe_layer_desc* L, const int32_t* token_ids, const uint16_t* x_bf16, int B, float* y, void* ws,
+                size_t ws_bytes, int32_t* idx_out, float* gw_out, void* const* events, void* stream) {
+  int st = check_layer(L, B);
+  if (st != MOE_OK) return st;
+  if ((st = check_ids(L, token_ids)) != MOE_OK) return st;
+  if (!x_bf16 || !y) return MOE_ERR_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(y, 16)) return MOE_ERR_ALIGN;
+  const size_t need = layer_ws_layout(B, L->d_model, L->d_ff, L->n_experts, L->top_k).total;
+  if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
+  if ((st = arch_check()) != MOE_OK) return st;
+  return layer_impl(L, x_bf16, B, y, nullptr, ws, idx_out, gw_out, events, (hipStream_t)stream, nullptr, nullptr,
+                    0.0, nullptr, token_ids);
+}
 }  // namespace
 
 extern "C" {
@@ -243,27 +269,40 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return MOE_OK;
 }
 
+
 int moe_layer_decode(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws, size_t ws_bytes,
                      int32_t* idx_out, float* gw_out, void* stream) {
-  return moe_layer_decode_profiled(L, x_bf16, B, y, ws, ws_bytes, idx_out, gw_out, nullptr, stream);
+  return layer_entry(L, nullptr, x_bf16, B, y, ws, ws_bytes, idx_out, gw_out, nullptr, stream);
+}
+
+int moe_layer_decode_ids(const moe_layer_desc* L, const int32_t* token_ids, const uint16_t* x_bf16, int B, float* y,
+                         void* ws, size_t ws_bytes, int32_t* idx_out, float* gw_out, void* stream) {
+  return layer_entry(L, token_ids, x_bf16, B, y, ws, ws_bytes, idx_out, gw_out, nullptr, stream);
+}
+
+int moe_workspace_flags(const void* ws, size_t ws_bytes, uint32_t* flags, void* stream) {
+  if (!ws || !flags) return MOE_ERR_ARG;
+  if (!aligned(ws, 256) || ws_bytes < (kCtrTimeout + 1) * sizeof(uint32_t)) return MOE_ERR_WORKSPACE;
+  uint32_t c[2] = {0u, 0u};
+  hipStream_t s = (hipStream_t)stream;
+  const uint32_t* ctr = static_cast<const uint32_t*>(ws);  // the counters region comes first
+  hipError_t e = hipMemcpyAsync(c, ctr + kCtrBadIds, sizeof(c), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e);
+  *flags = (c[1] ? 1u : 0u) | (c[0] ? 2u : 0u);
+  return MOE_OK;
 }
 
 int moe_layer_decode_profiled(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
                               size_t ws_bytes, int32_t* idx_out, float* gw_out, void* const* events, void* stream) {
-  int st = check_layer(L, B);
-  if (st != MOE_OK) return st;
-  if (!x_bf16 || !y) return MOE_ERR_ARG;
-  if (!aligned(x_bf16, 16) || !aligned(y, 16)) return MOE_ERR_ALIGN;
-  const size_t need = layer_ws_layout(B, L->d_model, L->d_ff, L->n_experts, L->top_k).total;
-  if ((st = check_ws(ws, ws_bytes, need)) != MOE_OK) return st;
-  if ((st = arch_check()) != MOE_OK) return st;
-  return layer_impl(L, x_bf16, B, y, nullptr, ws, idx_out, gw_out, events, (hipStream_t)stream);
+  return layer_entry(L, nullptr, x_bf16, B, y, ws, ws_bytes, idx_out, gw_out, events, stream);
 }
 
 int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
                             size_t ws_bytes, uint64_t* trace, int* trace_blocks, void* stream) {
   int st = check_layer(L, B);
   if (st != MOE_OK) return st;
+  if ((st = check_ids(L, nullptr)) != MOE_OK) return st;
   if (!x_bf16 || !y || !trace_blocks) return MOE_ERR_ARG;
   if (!aligned(x_bf16, 16) || !aligned(y, 16)) return MOE_ERR_ALIGN;
   const size_t need = layer_ws_layout(B, L->d_model, L->d_ff, L->n_experts, L->top_k).total;
@@ -288,11 +327,17 @@ size_t moe_stack_workspace_bytes(int B, int D, int F, int E, int top_k) {
 
 int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* h_in, int B, float* h_out, double eps,
                      void* ws, size_t ws_bytes, void* stream) {
+  return moe_stack_decode_ids(layers, n_layers, nullptr, h_in, B, h_out, eps, ws, ws_bytes, stream);
+}
+
+int moe_stack_decode_ids(const moe_layer_desc* layers, int n_layers, const int32_t* token_ids, const float* h_in,
+                         int B, float* h_out, double eps, void* ws, size_t ws_bytes, void* stream) {
   if (!layers || n_layers < 1 || !h_in || !h_out) return MOE_ERR_ARG;
   if (!(eps >= 0.0)) return MOE_ERR_ARG;
   int st;
   for (int l = 0; l < n_layers; ++l) {
     if ((st = check_layer(&layers[l], B)) != MOE_OK) return st;
+    if ((st = check_ids(&layers[l], token_ids)) != MOE_OK) return st;
     if (layers[l].d_model != layers[0].d_model || layers[l].d_ff != layers[0].d_ff ||
         layers[l].n_experts != layers[0].n_experts || layers[l].top_k != layers[0].top_k)
       return MOE_ERR_SHAPE;
@@ -315,7 +360,8 @@ int moe_stack_decode(const moe_layer_desc* layers, int n_layers, const float* h_
   const float* cur = h_in;
   for (int l = 0; l < n_layers; ++l) {
     float* dst = (n_layers - 1 - l) % 2 == 0 ? h_out : tmp;
-    st = layer_impl(&layers[l], nullptr, B, dst, cur, ws, nullptr, nullptr, nullptr, s, nullptr, cur, eps, xb);
+    st = layer_impl(&layers[l], nullptr, B, dst, cur, ws, nullptr, nullptr, nullptr, s, nullptr, cur, eps, xb,
+                    token_ids);
     if (st != MOE_OK) return st;
     cur = dst;
   }

@@ -111,7 +111,8 @@ int probe_xcd_count(uint32_t* scratch, int grid, hipStream_t s) {
 hipError_t launch_fused_layer(int fmt, int dfmt, const float* router_w, const uint16_t* x, const float* hn, double eps,
                               const WeightRef& gate, const WeightRef& up, const WeightRef& down, int E, int D, int Fd,
                               int k, int B, uint8_t* ws, const WsLayout& L, float* y, const float* residual,
-                              int32_t* idx_out, float* gw_out, uint64_t* trace, hipStream_t s) {
+                              int32_t* idx_out, float* gw_out, uint64_t* trace, hipStream_t s,
+                              const HashRoute& hr) {
   static_assert(kW == kRmsWaves, "the in-kernel norm sums over the norm kernel's eight waves");
   if (hn && (B != 1 || D > kFusedNormMaxD || D % 8 || hn == y)) return hipErrorInvalidValue;
   FusedArgs a;
@@ -119,6 +120,7 @@ hipError_t launch_fused_layer(int fmt, int dfmt, const float* router_w, const ui
   a.x = x;
   a.hn = hn;
   a.eps = eps;
+  a.hr = hr;
   a.gate = gate;
   a.up = up;
   a.down = down;

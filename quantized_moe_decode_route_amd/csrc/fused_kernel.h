@@ -172,6 +172,7 @@ struct FusedArgs {
   // into x = bf16_rne(h / sqrt(mean(h^2) + eps)) (B = 1, d_model <= 4096).
   const float* hn;
   double eps;
+  HashRoute hr;  // table set: hash-routed layer
   WeightRef gate, up, down;
   uint8_t* ws;
   WsLayout L;
@@ -453,107 +454,136 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // wave t handles token t.  Each lane sorts its four candidates; every round
   // takes the wave-wide best of the lanes' heads and the owner pops it.
   for (int t = w; t < B; t += kW) {
-    constexpr int kPer = MOE_MAX_EXPERTS / kWave;
-    uint64_t hw[kPer], lw[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int id = lane + kWave * i;
-      if (id < E) {
-        const uint64_t* p = lg + ((int64_t)t * E + id) * 2;
-        hw[i] = ld_dev(p);
-        lw[i] = ld_dev(p + 1);
-      }
-    }
-    {
-      uint64_t wv[2 * kPer];
-      bool valid[2 * kPer];
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        wv[2 * i] = hw[i];
-        wv[2 * i + 1] = lw[i];
-        valid[2 * i] = valid[2 * i + 1] = lane + kWave * i < E;
-      }
-      const int rr = await_tags<2 * kPer>(
-          [&](int j) { return lg + ((int64_t)t * E + lane + kWave * (j >> 1)) * 2 + (j & 1); }, wv, valid, tag,
-          wall_clock64(), &s_timeout);
-      if (a.trace && threadIdx.x == 0) trace_rereads = rr;
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        hw[i] = wv[2 * i];
-        lw[i] = wv[2 * i + 1];
-      }
-    }
-    if (t == 0) stamp(a, 3);
-    double v[kPer];
-    int id[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      id[i] = lane + kWave * i;
-      v[i] = -__builtin_inf();
-      if (id[i] < E) {
-        v[i] = __hiloint2double((int)payload_of(hw[i]), (int)payload_of(lw[i]));
-      } else {
-        id[i] = 0x7FFFFFFF;
-      }
-    }
-    auto cswap = [&](int p, int q) {
-      if (better(v[q], id[q], v[p], id[p])) {
-        const double tv = v[p];
-        const int ti = id[p];
-        v[p] = v[q];
-        id[p] = id[q];
-        v[q] = tv;
-        id[q] = ti;
-      }
-    };
-    cswap(0, 1);
-    cswap(2, 3);
-    cswap(0, 2);
-    cswap(1, 3);
-    cswap(1, 2);
-    // Each round: the largest head by the top 32 bits of its order-preserving
-    // key (one DPP max); when a single lane holds that key its head is the
-    // exact winner, else the tied lanes' heads are compared exactly.
     double my_v = 0.0;  // lane r keeps the rank-r selection
     int my_i = 0;
-    for (int r = 0; r < k; ++r) {
-      const uint32_t key = order_key32(v[0] + 0.0);  // -0.0 compares equal to +0.0
-      const uint32_t top_key = wave_max_u32(key);
-      const uint64_t tied = __ballot(key == top_key);
-      double bv;
-      int bi;
-      if (__popcll(tied) == 1) {
-        const int L = (int)__builtin_ctzll(tied);
-        bv = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v[0]), L),
-                              __builtin_amdgcn_readlane(__double2loint(v[0]), L));
-        bi = __builtin_amdgcn_readlane(id[0], L);
-      } else {
-        bv = key == top_key ? v[0] : -__builtin_inf();
-        bi = key == top_key ? id[0] : 0x7FFFFFFF;
-        wave_argmax(bv, bi);
+    if (a.hr.table) {
+      // Hash-routed layer: the token's experts come from its table row, in
+      // rank order; only their logits are read from the exchange.
+      bool bad;
+      my_i = hash_expert(a.hr, t, E, k, lane, bad);
+      if (bad && lane == 0)
+        __hip_atomic_fetch_or(ctr + kCtrBadIds, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint64_t* p = lg + ((int64_t)t * E + my_i) * 2;
+      uint64_t wv[2];
+      const bool valid[2] = {lane < k, lane < k};
+      wv[0] = lane < k ? ld_dev(p) : 0ull;
+      wv[1] = lane < k ? ld_dev(p + 1) : 0ull;
+      const int rr = await_tags<2>([&](int j) { return p + j; }, wv, valid, tag, wall_clock64(), &s_timeout);
+      if (a.trace && threadIdx.x == 0) trace_rereads = rr;
+      if (t == 0) stamp(a, 3);
+      if (lane < k) my_v = __hiloint2double((int)payload_of(wv[0]), (int)payload_of(wv[1]));
+      if (B == 1) {  // for the prefetching waves
+        if (lane < k) reinterpret_cast<volatile int*>(s_pre)[lane] = my_i;
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) *reinterpret_cast<volatile int*>(&s_pre_n) = k;
       }
-      if (lane == r) {
-        my_v = bv;
-        my_i = bi;
+    } else {
+      constexpr int kPer = MOE_MAX_EXPERTS / kWave;
+      uint64_t hw[kPer], lw[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int id = lane + kWave * i;
+        if (id < E) {
+          const uint64_t* p = lg + ((int64_t)t * E + id) * 2;
+          hw[i] = ld_dev(p);
+          lw[i] = ld_dev(p + 1);
+        }
       }
-      if (B == 1 && lane == 0) {  // for the prefetching waves
-        reinterpret_cast<volatile int*>(s_pre)[r] = min(max(bi, 0), E - 1);
-        *reinterpret_cast<volatile int*>(&s_pre_n) = r + 1;
+      {
+        uint64_t wv[2 * kPer];
+        bool valid[2 * kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          wv[2 * i] = hw[i];
+          wv[2 * i + 1] = lw[i];
+          valid[2 * i] = valid[2 * i + 1] = lane + kWave * i < E;
+        }
+        const int rr = await_tags<2 * kPer>(
+            [&](int j) { return lg + ((int64_t)t * E + lane + kWave * (j >> 1)) * 2 + (j & 1); }, wv, valid, tag,
+            wall_clock64(), &s_timeout);
+        if (a.trace && threadIdx.x == 0) trace_rereads = rr;
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          hw[i] = wv[2 * i];
+          lw[i] = wv[2 * i + 1];
+        }
       }
-      if (id[0] == bi) {  // this lane held the winner: pop it
-        v[0] = v[1];
-        id[0] = id[1];
-        v[1] = v[2];
-        id[1] = id[2];
-        v[2] = v[3];
-        id[2] = id[3];
-        v[3] = -__builtin_inf();
-        id[3] = 0x7FFFFFFF;
+      if (t == 0) stamp(a, 3);
+      double v[kPer];
+      int id[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        id[i] = lane + kWave * i;
+        v[i] = -__builtin_inf();
+        if (id[i] < E) {
+          v[i] = __hiloint2double((int)payload_of(hw[i]), (int)payload_of(lw[i]));
+        } else {
+          id[i] = 0x7FFFFFFF;
+        }
+      }
+      auto cswap = [&](int p, int q) {
+        if (better(v[q], id[q], v[p], id[p])) {
+          const double tv = v[p];
+          const int ti = id[p];
+          v[p] = v[q];
+          id[p] = id[q];
+          v[q] = tv;
+          id[q] = ti;
+        }
+      };
+      cswap(0, 1);
+      cswap(2, 3);
+      cswap(0, 2);
+      cswap(1, 3);
+      cswap(1, 2);
+      // Each round: the largest head by the top 32 bits of its order-preserving
+      // key (one DPP max); when a single lane holds that key its head is the
+      // exact winner, else the tied lanes' heads are compared exactly.
+      for (int r = 0; r < k; ++r) {
+        const uint32_t key = order_key32(v[0] + 0.0);  // -0.0 compares equal to +0.0
+        const uint32_t top_key = wave_max_u32(key);
+        const uint64_t tied = __ballot(key == top_key);
+        double bv;
+        int bi;
+        if (__popcll(tied) == 1) {
+          const int L = (int)__builtin_ctzll(tied);
+          bv = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v[0]), L),
+                                __builtin_amdgcn_readlane(__double2loint(v[0]), L));
+          bi = __builtin_amdgcn_readlane(id[0], L);
+        } else {
+          bv = key == top_key ? v[0] : -__builtin_inf();
+          bi = key == top_key ? id[0] : 0x7FFFFFFF;
+          wave_argmax(bv, bi);
+        }
+        if (lane == r) {
+          my_v = bv;
+          my_i = bi;
+        }
+        if (B == 1 && lane == 0) {  // for the prefetching waves
+          reinterpret_cast<volatile int*>(s_pre)[r] = min(max(bi, 0), E - 1);
+          *reinterpret_cast<volatile int*>(&s_pre_n) = r + 1;
+        }
+        if (id[0] == bi) {  // this lane held the winner: pop it
+          v[0] = v[1];
+          id[0] = id[1];
+          v[1] = v[2];
+          id[1] = id[2];
+          v[2] = v[3];
+          id[2] = id[3];
+          v[3] = -__builtin_inf();
+          id[3] = 0x7FFFFFFF;
+        }
       }
     }
-    // Softmax over the k selected logits, summed in rank order.
-    const double top = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_v), 0),
-                                        __builtin_amdgcn_readlane(__double2loint(my_v), 0));
+    // Softmax over the k selected logits, summed in rank order, shifted by
+    // their maximum (rank 0's logit when they come from the top-k).
+    double top = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_v), 0),
+                                  __builtin_amdgcn_readlane(__double2loint(my_v), 0));
+    if (a.hr.table) {
+      for (int r = 1; r < k; ++r)
+        top = fmax(top, __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_v), r),
+                                         __builtin_amdgcn_readlane(__double2loint(my_v), r)));
+    }
     const double ex = lane < k ? exp(my_v - top) : 0.0;
     double sum = 0.0;
     for (int r = 0; r < k; ++r)

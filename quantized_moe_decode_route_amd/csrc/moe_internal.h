@@ -279,8 +279,33 @@ enum : int {
   kCtrRoute = 0,     // arrivals in the stand-alone routing kernel (reset by its last workgroup)
   kCtrEpoch = 16,    // number of the last completed single-launch call (tags of a call = epoch + 1)
   kCtrXcdBase = 32,  // [16]: per-XCD arrival counters of the single-launch layer
+  kCtrBadIds = 62,   // set if a hash-routed layer met an invalid token id or table row (sticky, like the next)
   kCtrTimeout = 63,  // set if a bounded wait gave up; stays set until the workspace is re-initialised
 };
+
+// ---------------------------------------------------------------- hash routing
+// A hash-routed layer takes each token's experts from a table indexed by its
+// token id instead of from the router's top-k.
+struct HashRoute {
+  const int32_t* table;  // int32 [vocab][k]; null: learned routing
+  const int32_t* ids;    // int32 [B] token ids
+  int vocab;
+};
+
+// Lane r < k: the rank-r expert of token t.  An id outside [0, vocab) or a
+// row with an expert outside [0, E) or a repeated one makes the token use
+// experts 0..k-1 and raises `bad` (uniform over the wave).  Every lane of
+// the wave must call it.
+__device__ __forceinline__ int hash_expert(const HashRoute& h, int t, int E, int k, int lane, bool& bad) {
+  int id = h.ids[t];
+  const bool bad_id = id < 0 || id >= h.vocab;
+  id = bad_id ? 0 : id;
+  const int e = lane < k ? h.table[(int64_t)id * k + lane] : 0;
+  bool mine = lane < k && (e < 0 || e >= E);
+  for (int i = 0; i + 1 < k; ++i) mine |= lane < k && lane > i && e == __builtin_amdgcn_readlane(e, i);
+  bad = bad_id || __ballot(mine) != 0ull;
+  return bad ? (lane < k ? lane : 0) : e;
+}
 
 // ---------------------------------------------------------------- launchers
 // Each returns a hipError_t (hipSuccess on success).
@@ -308,7 +333,7 @@ hipError_t launch_gemv(int fmt, const void* w0, const uint16_t* scale, int N, in
 
 hipError_t launch_route(const float* router_w, int E, int D, const uint16_t* x_bf16, int B, int k,
                         uint8_t* ws, const WsLayout& L, int32_t* idx_out, float* gw_out,
-                        double* logits_out, hipStream_t s);
+                        double* logits_out, hipStream_t s, const HashRoute& hr = HashRoute{});
 
 hipError_t launch_gate_up(int fmt, const WeightRef& gate, const WeightRef& up, int D, int F, int B,
                           int k, uint8_t* ws, const WsLayout& L, hipStream_t s);
@@ -355,7 +380,8 @@ int xcd_count();
 hipError_t launch_fused_layer(int fmt, int dfmt, const float* router_w, const uint16_t* x, const float* hn, double eps,
                               const WeightRef& gate, const WeightRef& up, const WeightRef& down, int E, int D, int Fd,
                               int k, int B, uint8_t* ws, const WsLayout& L, float* y, const float* residual,
-                              int32_t* idx_out, float* gw_out, uint64_t* trace, hipStream_t s);
+                              int32_t* idx_out, float* gw_out, uint64_t* trace, hipStream_t s,
+                              const HashRoute& hr = HashRoute{});
 constexpr int kFusedNormMaxD = 4096;
 
 }  // namespace moe

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ wr
                                                     const uint16_t* __restrict__ xb, int B, int k,
                                                     uint8_t* __restrict__ ws, WsLayout L,
                                                     int32_t* __restrict__ idx_out, float* __restrict__ gw_out,
-                                                    double* __restrict__ logits_out) {
+                                                    double* __restrict__ logits_out, HashRoute hr) {
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
   double* logits = reinterpret_cast<double*>(ws + L.logits);
@@ -75,6 +75,24 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ wr
   // Top-k per token: one wave per token (tokens wave, wave+4).
   for (int t = wave; t < B; t += kRouteWaves) {
     const double* lt = logits + (int64_t)t * E;
+    if (hr.table) {  // hash-routed: the table's experts, weighted by their logits
+      bool bad;
+      const int my_i = hash_expert(hr, t, E, k, lane, bad);
+      if (bad && lane == 0)
+        __hip_atomic_fetch_or(reinterpret_cast<uint32_t*>(ws + L.counters) + kCtrBadIds, 1u, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+      const double my_v = lane < k ? lt[my_i] : 0.0;
+      double top = -__builtin_inf();  // softmax over the k logits, shifted by their maximum
+      for (int r = 0; r < k; ++r) top = fmax(top, __shfl(my_v, r, kWave));
+      const double ex = lane < k ? exp(my_v - top) : 0.0;
+      double sum = 0.0;
+      for (int r = 0; r < k; ++r) sum += __shfl(ex, r, kWave);
+      if (lane < k) {
+        s_idx[t * k + lane] = my_i;
+        s_gw[t * k + lane] = (float)(ex / sum);
+      }
+      continue;
+    }
     constexpr int kPer = MOE_MAX_EXPERTS / kWave;  // 4 logits per lane
     double v[kPer];
     int id[kPer];
@@ -187,10 +205,11 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ wr
 }  // namespace
 
 hipError_t launch_route(const float* router_w, int E, int D, const uint16_t* x_bf16, int B, int k, uint8_t* ws,
-                        const WsLayout& L, int32_t* idx_out, float* gw_out, double* logits_out, hipStream_t s) {
+                        const WsLayout& L, int32_t* idx_out, float* gw_out, double* logits_out, hipStream_t s,
+                        const HashRoute& hr) {
   dim3 grid((E + kRouteWaves - 1) / kRouteWaves);
   hipLaunchKernelGGL(route_kernel, grid, dim3(kRouteWaves * kWave), 0, s, router_w, E, D, x_bf16, B, k, ws, L,
-                     idx_out, gw_out, logits_out);
+                     idx_out, gw_out, logits_out, hr);
   return hipGetLastError();
 }
 

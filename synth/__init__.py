@@ -181,6 +181,18 @@ def router_weights(seed: int, layer: int, n_experts: int, d_model: int) -> np.nd
                       (n_experts, d_model), 0.02)
 
 
+def tid2eid_table(seed: int, vocab: int, n_experts: int, top_k: int) -> np.ndarray:
+    """A stand-in hash table for hash-routed layers: row t holds top_k distinct
+    experts of token id t, drawn from a seeded permutation (the pages do not
+    give the hash function)."""
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.permutation(n_experts)[:top_k] for _ in range(vocab)]).astype(np.int32)
+
+
+def token_ids(seed: int, n_tokens: int, vocab: int) -> np.ndarray:
+    return np.random.default_rng(seed).integers(0, vocab, size=n_tokens).astype(np.int32)
+
+
 def token_bf16(token_seed: int, n_tokens: int, d_model: int) -> np.ndarray:
     """Activations bf16 bits [n_tokens, d_model] ~ N(0, 1) rounded to bfloat16."""
     return bf16_bits_from_f32(normal_f32(token_seed, (n_tokens, d_model), 1.0))

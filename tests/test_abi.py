@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert moe.moe_abi_version() == moe.ABI_VERSION == 4
+    assert moe.moe_abi_version() == moe.ABI_VERSION == 5
     for st in range(7):
         assert moe.moe_status_string(st)
     assert moe.moe_status_string(0) == "ok"
@@ -123,6 +123,28 @@ def test_mixed_format_validation_on_host(L):
     assert run() == 6
     d.down_stride, d.down_format = 2752512, 3           # INT4 down needs its scales
     assert run() == 1
+
+
+def test_hash_routing_validation_on_host(L):
+    """A hash-routed layer (tid2eid set) needs the tokens' ids."""
+    d = moe.make_layer_desc("mxfp4", FAKE, FAKE, FAKE, FAKE, 256, 4096, 2048, 6, 4456704, 4456704, 4456704,
+                            tid2eid=FAKE, vocab=1000)
+    ws_ok = 1 << 30
+    layer = lambda ids: L.moe_layer_decode_ids(ctypes.byref(d), ids, FAKE, 1, FAKE, FAKE, ws_ok, None, None, None)
+    assert L.moe_layer_decode(ctypes.byref(d), FAKE, 1, FAKE, FAKE, ws_ok, None, None, None) == 1  # no ids
+    assert layer(None) == 1
+    assert layer(FAKE + 2) == 6                                  # ids 4-byte aligned
+    d.vocab = 0
+    assert layer(FAKE) == 1                                      # an empty table
+    d.vocab, d.tid2eid = 1000, FAKE + 2
+    assert layer(FAKE) == 6                                      # table 4-byte aligned
+    d.tid2eid = FAKE
+    arr = (moe.moe_layer_desc * 1)(d)
+    assert L.moe_stack_decode(arr, 1, FAKE, 1, FAKE, 1e-6, FAKE, ws_ok, None) == 1
+    assert L.moe_stack_decode_ids(arr, 1, None, FAKE, 1, FAKE, 1e-6, FAKE, ws_ok, None) == 1
+    f = ctypes.c_uint32(0)
+    assert L.moe_workspace_flags(None, ws_ok, ctypes.byref(f), None) == 1
+    assert L.moe_workspace_flags(FAKE + 16, ws_ok, ctypes.byref(f), None) == 5  # workspaces are 256-aligned
 
 
 def test_layout_validation_on_host(L):

@@ -571,3 +571,61 @@ def test_int4_scale_invariance_and_rounding_properties():
         e_plain = np.sum((w[i] - qq * np.float64(s1_)) ** 2)
         e_best = np.sum((w[i] - qv * s) ** 2)
         assert e_best <= e_plain * (1 + 1e-12)
+
+
+# ---------------------------------------------------------------- hash-routed layers
+
+def test_hash_route_closed_form():
+    """Experts come from the table row in its order; the weights are the
+    softmax of their logits: logits ln(1..8) give weights proportional to
+    the chosen experts' 1+index ("cabbage v4x quant surgery", hash layers)."""
+    l = np.log(np.arange(1, 9, dtype=np.float64))[None, :]
+    table = np.array([[7, 0, 2], [1, 3, 5]], dtype=np.int32)
+    idx, g, nb = oracle.hash_route(l, 3, table, np.array([0], dtype=np.int32))
+    assert nb == 0 and idx.tolist() == [[7, 0, 2]]
+    np.testing.assert_allclose(g[0], np.array([8.0, 1.0, 3.0]) / 12.0, rtol=1e-15)
+    idx, g, _ = oracle.hash_route(np.vstack([l, l + 50.0]), 3, table, np.array([1, 1], dtype=np.int32))
+    assert idx.tolist() == [[1, 3, 5], [1, 3, 5]]
+    np.testing.assert_allclose(g[1], g[0], rtol=1e-14)   # softmax: a common shift changes nothing
+    np.testing.assert_allclose(g[0], np.array([2.0, 4.0, 6.0]) / 12.0, rtol=1e-15)
+
+
+def test_hash_route_equals_learned_route_on_its_own_choice():
+    """A table row that holds a token's learned top-k (in rank order) gives
+    exactly the learned routing's weights (same shift, same order): a check
+    against the independent top-k routine."""
+    rng = np.random.default_rng(12)
+    logits = rng.standard_normal((5, 40))
+    idx_l, g_l = oracle.topk_softmax(logits, 6)
+    table = idx_l.astype(np.int32)                      # vocab 5: token id b -> row b
+    idx_h, g_h, nb = oracle.hash_route(logits, 6, table, np.arange(5, dtype=np.int32))
+    assert nb == 0
+    assert np.array_equal(idx_h, idx_l)
+    assert np.array_equal(g_h, g_l)
+
+
+def test_hash_route_invalid_ids_and_rows():
+    l = np.zeros((4, 16))
+    table = np.array([[3, 4, 5], [3, 3, 5], [3, 16, 5]], dtype=np.int32)
+    idx, g, nb = oracle.hash_route(l, 3, table, np.array([0, 1, 2, 7], dtype=np.int32))
+    assert nb == 3                                       # repeated expert, expert >= E, id >= vocab
+    assert idx.tolist() == [[3, 4, 5], [0, 1, 2], [0, 1, 2], [0, 1, 2]]
+    np.testing.assert_allclose(g, 1.0 / 3.0, rtol=1e-15)
+
+
+def test_hashed_layer_composition():
+    """A hash-routed layer is the learned layer's expert FFN and combine with
+    the table's experts: with a table holding the learned choice it gives the
+    learned layer's result exactly."""
+    rng = np.random.default_rng(13)
+    E, D, F, k = 6, 64, 64, 2
+    experts = {e: (_rand_mx(F, D, rng), _rand_mx(F, D, rng), _rand_mx(D, F, rng)) for e in range(E)}
+    wr = (rng.standard_normal((E, D)) * 0.05).astype(np.float32)
+    xb = (rng.standard_normal((1, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    _, _, logits = oracle.route_topk(wr, xb, k)
+    learned_idx, _ = oracle.topk_softmax(logits, k)
+    table = learned_idx.astype(np.int32)
+    y_h, i_h, g_h = oracle.layer_decode("mxfp4", lambda e: experts[e], wr, xb, k, F,
+                                        hashed=(table, np.array([0], dtype=np.int32)))
+    y_l, i_l, g_l = oracle.layer_decode("mxfp4", lambda e: experts[e], wr, xb, k, F)
+    assert np.array_equal(i_h, i_l) and np.array_equal(g_h, g_l) and np.array_equal(y_h, y_l)
