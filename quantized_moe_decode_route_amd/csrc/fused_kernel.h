@@ -13,13 +13,16 @@
 // dispatcher used.
 //
 //  1. Routing.  Workgroup g computes expert g's router logits for every token
-//     (fp64) and publishes them device-wide.  Every workgroup gathers all
+//     (fp64) and publishes them device-wide; in a layer stack at B=1 it first
+//     RMS-normalises the residual stream itself.  Every workgroup gathers all
 //     logits and derives, identically, each token's top-k (largest first, ties
-//     to the lower index), the softmax weights and the grouping of
-//     (token, rank) pairs by expert.
+//     to the lower index) -- or, in a hash-routed layer, reads the token's
+//     experts from its table row and only their logits -- the softmax
+//     weights and the grouping of (token, rank) pairs by expert.
 //  2. Gate/up.  XCD x owns the d_ff slice [x*F/NX, (x+1)*F/NX): its workgroups
 //     compute h = SiLU(gate.x) * (up.x) for those rows of every selected
 //     expert, keeping the next experts' blocks in flight, and publish h.
+//     Gate and up may be in another format than down (template F vs FD).
 //  3. Down.  XCD x requests its first experts' down blocks, gathers its own h
 //     slice, multiplies every down row's slice-x columns by it (partial sums
 //     over d_ff), combines the k ranks of each token in rank order, and
@@ -1025,7 +1028,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
   };
   // Gate/up work items are (expert group, row) pairs of this workgroup's
-  // rows, groups ascending, handed out by an LDS counter: a wave takes its
+  // rows, in group-table order (experts ascending; at B=1 in rank order),
+  // handed out by an LDS counter: a wave takes its
   // next item when it requests the item's weights (kRingGU - 1 items ahead),
   // so waves that get their data sooner take more items and all finish
   // together.  A wave's first pass also requests the down prologue between
