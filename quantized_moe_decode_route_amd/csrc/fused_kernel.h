@@ -103,6 +103,18 @@ __device__ __forceinline__ float group_sum_dpp(float v) {
 
 
 // (value, index) with "better" = larger value, then lower index.
+// LDS words polled by other waves of the workgroup: relaxed workgroup-scope
+// atomics, which stay ds_read/ds_write (a volatile access through a generic
+// pointer becomes a flat access, which the compiler then waits for together
+// with every outstanding global load).  One wave's LDS operations complete in
+// issue order, so a reader that sees a count also sees the entries before it.
+__device__ __forceinline__ void lds_put(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ int lds_get(int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 __device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
@@ -476,9 +488,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       if (t == 0) stamp(a, 3);
       if (lane < k) my_v = __hiloint2double((int)payload_of(wv[0]), (int)payload_of(wv[1]));
       if (B == 1) {  // for the prefetching waves
-        if (lane < k) reinterpret_cast<volatile int*>(s_pre)[lane] = my_i;
+        if (lane < k) lds_put(&s_pre[lane], my_i);
         __builtin_amdgcn_wave_barrier();
-        if (lane == 0) *reinterpret_cast<volatile int*>(&s_pre_n) = k;
+        if (lane == 0) lds_put(&s_pre_n, k);
       }
     } else {
       constexpr int kPer = MOE_MAX_EXPERTS / kWave;
@@ -563,8 +575,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
           my_i = bi;
         }
         if (B == 1 && lane == 0) {  // for the prefetching waves
-          reinterpret_cast<volatile int*>(s_pre)[r] = min(max(bi, 0), E - 1);
-          *reinterpret_cast<volatile int*>(&s_pre_n) = r + 1;
+          lds_put(&s_pre[r], min(max(bi, 0), E - 1));
+          lds_put(&s_pre_n, r + 1);
         }
         if (id[0] == bi) {  // this lane held the winner: pop it
           v[0] = v[1];
@@ -600,45 +612,6 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       atomicOr(&s_mask[my_i], (1u << t) | ((uint32_t)lane << (8 + 3 * t)));
     }
   }
-  // One token: while wave 0 selects the experts, the other waves pull this
-  // workgroup's gate/up rows of the first ones into the XCD's L2 (taking the
-  // workgroup's likely place in the XCD from its index: a wrong guess only
-  // prefetches another workgroup's rows), so the first gate/up loads find
-  // them there.  The loaded bytes are kept until after gate/up, whose waits
-  // cover these older loads anyway.
-  uint32_t pre_sink = 0u;
-  if constexpr (std::is_same<F, MxFmt>::value) {
-    if (B == 1 && w >= 1) {
-      const int FSp = Fd / NX, RPWp = (FSp + GX - 1) / GX;
-      const int fr = xcd * FSp + ((int)(blockIdx.x / NX) % GX) * RPWp;
-      const int rows = min(RPWp, xcd * FSp + FSp - fr);
-      const int64_t rb = (int64_t)(D / 32) * 17;  // bytes per row
-      const int64_t nbytes = rows > 0 ? rows * rb : 0;
-      const int lines = (int)((nbytes + 127) / 128);
-      const int p = (int)threadIdx.x - kWave;
-      const uint64_t t0 = wall_clock64();
-      for (int r = 0; r < min(k, kPrefetchExperts) && lines > 0; ++r) {
-        while (*reinterpret_cast<volatile int*>(&s_pre_n) <= r && wall_clock64() - t0 < kSpinTicks)
-          __builtin_amdgcn_s_sleep(1);
-        const int e = reinterpret_cast<volatile int*>(s_pre)[r];
-        if (p < 2 * lines) {
-          const WeightRef& m = p < lines ? a.gate : a.up;
-          const int64_t off = min((int64_t)(p < lines ? p : p - lines) * 128, nbytes - 1);
-          pre_sink += m.base[e * m.stride + fr * rb + off];
-        } else if (kPrefetchDown && DNK == 2 && a.down.layout == MOE_LAYOUT_MFMA16 && Fd / NX == 256) {
-          // the expert's down blocks of this slice for the workgroup's output
-          // rows: one contiguous run in the MOE_LAYOUT_MFMA16 order
-          const int RPWdp = (D + GX - 1) / GX;
-          const int nd0 = ((int)(blockIdx.x / NX) % GX) * RPWdp;
-          const int q = p - 2 * lines;
-          if (RPWdp % 16 == 0 && nd0 + RPWdp <= D && q * 128 < RPWdp * 8 * 17) {
-            const int64_t blk = mfma16_block(nd0, xcd * 8, D);
-            pre_sink += a.down.base[e * a.down.stride + blk * 17 + q * 128];
-          }
-        }
-      }
-    }
-  }
   if (threadIdx.x == 0) {  // the arrival counter has long returned by now
     s_jx = (int)(xcd_arrival % (uint32_t)GX);
     if (a.trace) {
@@ -665,6 +638,53 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
       for (int c = 0; c < kCh; ++c)
         xl[(t * kCh + c) * UG + u] = make_uint4(xs[4 * c], xs[4 * c + 1], xs[4 * c + 2], xs[4 * c + 3]);
+    }
+  }
+  // One token: while wave 0 selects the experts, the other waves pull this
+  // workgroup's gate/up rows of the first ones into the XCD's L2 (taking the
+  // workgroup's likely place in the XCD from its index: a wrong guess only
+  // prefetches another workgroup's rows), so the first gate/up loads find
+  // them there.  Every lane issues one dword load per expert (lanes with no
+  // line of their own read the gate tensor's first dword); the values are
+  // only consumed after gate/up, whose waits cover these older loads, so no
+  // wave waits for them before the barrier below.
+  uint32_t pre_sink[kPrefetchExperts];
+#pragma unroll
+  for (int r = 0; r < kPrefetchExperts; ++r) pre_sink[r] = 0u;
+  if constexpr (std::is_same<F, MxFmt>::value) {
+    if (B == 1 && w >= 1) {
+      const int FSp = Fd / NX, RPWp = (FSp + GX - 1) / GX;
+      const int fr = xcd * FSp + ((int)(blockIdx.x / NX) % GX) * RPWp;
+      const int rows = min(RPWp, xcd * FSp + FSp - fr);
+      const int64_t rb = (int64_t)(D / 32) * 17;  // bytes per row
+      const int64_t nbytes = rows > 0 ? rows * rb : 0;
+      const int lines = (int)((nbytes + 127) / 128);
+      const int p = (int)threadIdx.x - kWave;
+      const uint64_t t0 = wall_clock64();
+#pragma unroll
+      for (int r = 0; r < kPrefetchExperts; ++r) {
+        if (r < k && lines > 0) {
+          while (lds_get(&s_pre_n) <= r && wall_clock64() - t0 < kSpinTicks)
+            __builtin_amdgcn_s_sleep(1);
+          const int e = lds_get(&s_pre[r]);
+          const uint8_t* q8 = a.gate.base;
+          if (p < 2 * lines) {
+            const WeightRef& m = p < lines ? a.gate : a.up;
+            const int64_t off = min((int64_t)(p < lines ? p : p - lines) * 128, nbytes - 1);
+            q8 = m.base + e * m.stride + fr * rb + off;
+          } else if (kPrefetchDown && DNK == 2 && a.down.layout == MOE_LAYOUT_MFMA16 && Fd / NX == 256) {
+            // the expert's down blocks of this slice for the workgroup's output
+            // rows: one contiguous run in the MOE_LAYOUT_MFMA16 order
+            const int RPWdp = (D + GX - 1) / GX;
+            const int nd0 = ((int)(blockIdx.x / NX) % GX) * RPWdp;
+            const int q = p - 2 * lines;
+            if (RPWdp % 16 == 0 && nd0 + RPWdp <= D && q * 128 < RPWdp * 8 * 17)
+              q8 = a.down.base + e * a.down.stride + mfma16_block(nd0, xcd * 8, D) * 17 + q * 128;
+          }
+          q8 -= reinterpret_cast<uintptr_t>(q8) & 3;  // pointer arithmetic keeps it a global load
+          pre_sink[r] = *reinterpret_cast<const uint32_t*>(q8);
+        }
+      }
     }
   }
   if constexpr (DNK > 0) {  // the zero B operand (slot S) read by lanes without a token
@@ -1135,7 +1155,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     while (item[kRingGU - 1] < NI) pass(std::false_type{});
   }
   stamp(a, 6);
-  asm volatile("" ::"v"(pre_sink));  // the prefetched bytes, long since arrived
+#pragma unroll
+  for (int r = 0; r < kPrefetchExperts; ++r) asm volatile("" ::"v"(pre_sink[r]));  // long since arrived
   fill_slot_tables();
 
   // ---------------------------------------------------------------- 3. down (partials over the slice)
