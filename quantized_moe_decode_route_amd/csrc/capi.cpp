@@ -112,7 +112,7 @@ WeightRef wref(const void* base, int64_t stride, const uint16_t* scale, int64_t 
 int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, const float* residual, void* ws,
                int32_t* idx_out, float* gw_out, void* const* events, hipStream_t s, uint64_t* trace = nullptr,
                const float* hn = nullptr, double eps = 0.0, uint16_t* xbuf = nullptr,
-               const int32_t* token_ids = nullptr) {
+               const int32_t* token_ids = nullptr, const float* next_router = nullptr) {
   const HashRoute hr{L->tid2eid, token_ids, L->vocab};
   const int D = L->d_model, F = L->d_ff, E = L->n_experts, k = L->top_k;
   const WsLayout W = layer_ws_layout(B, D, F, E, k);
@@ -142,7 +142,7 @@ int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
   }
   if (fused) {
     e = launch_fused_layer(L->format, fd, L->router_w, x_bf16, hn, eps, g, u, d, E, D, F, k, B, w, W, y, residual,
-                           idx_out, gw_out, trace, s, hr);
+                           idx_out, gw_out, trace, s, hr, next_router);
     if (e != hipSuccess) return hip_status(e);
   } else {
     if ((e = launch_route(L->router_w, E, D, x_bf16, B, k, w, W, idx_out, gw_out, nullptr, s, hr)) != hipSuccess)
@@ -360,8 +360,10 @@ int moe_stack_decode_ids(const moe_layer_desc* layers, int n_layers, const int32
   const float* cur = h_in;
   for (int l = 0; l < n_layers; ++l) {
     float* dst = (n_layers - 1 - l) % 2 == 0 ? h_out : tmp;
+    // (layers of one stack share E and d_model, so layer l can pull its row
+    // of layer l+1's router into L2)
     st = layer_impl(&layers[l], nullptr, B, dst, cur, ws, nullptr, nullptr, nullptr, s, nullptr, cur, eps, xb,
-                    token_ids);
+                    token_ids, l + 1 < n_layers ? layers[l + 1].router_w : nullptr);
     if (st != MOE_OK) return st;
     cur = dst;
   }

@@ -112,7 +112,7 @@ hipError_t launch_fused_layer(int fmt, int dfmt, const float* router_w, const ui
                               const WeightRef& gate, const WeightRef& up, const WeightRef& down, int E, int D, int Fd,
                               int k, int B, uint8_t* ws, const WsLayout& L, float* y, const float* residual,
                               int32_t* idx_out, float* gw_out, uint64_t* trace, hipStream_t s,
-                              const HashRoute& hr) {
+                              const HashRoute& hr, const float* next_router) {
   static_assert(kW == kRmsWaves, "the in-kernel norm sums over the norm kernel's eight waves");
   if (hn && (B != 1 || D > kFusedNormMaxD || D % 8 || hn == y)) return hipErrorInvalidValue;
   FusedArgs a;
@@ -121,6 +121,7 @@ hipError_t launch_fused_layer(int fmt, int dfmt, const float* router_w, const ui
   a.hn = hn;
   a.eps = eps;
   a.hr = hr;
+  a.next_router = next_router;
   a.gate = gate;
   a.up = up;
   a.down = down;

@@ -188,6 +188,9 @@ struct FusedArgs {
   const float* hn;
   double eps;
   HashRoute hr;  // table set: hash-routed layer
+  // Layer stack: the router weights of the layer that runs next (same E and
+  // D), or null.  Workgroup g pulls its row g into L2 while it waits for h.
+  const float* next_router;
   WeightRef gate, up, down;
   uint8_t* ws;
   WsLayout L;
@@ -1158,6 +1161,13 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
   for (int r = 0; r < kPrefetchExperts; ++r) asm volatile("" ::"v"(pre_sink[r]));  // long since arrived
   fill_slot_tables();
+  // Layer stack: while this workgroup waits for the XCD's h slice, its row of
+  // the next layer's router goes to L2 (one load per 128-byte line); the
+  // next launch has the same grid, so its workgroup g runs on this XCD and
+  // finds the row there.  The value is only consumed at the end.
+  uint32_t nr_sink = 0u;
+  if (a.next_router && g < E && (int)threadIdx.x * 32 < D)
+    nr_sink = *reinterpret_cast<const uint32_t*>(a.next_router + (int64_t)g * D + 32 * threadIdx.x);
 
   // ---------------------------------------------------------------- 3. down (partials over the slice)
   if constexpr (DNK == 0) {
@@ -1293,6 +1303,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     // (workgroup 0 consumed the logits of all of them), so advance it.
     if (g == 0) ctr[kCtrEpoch] = tag;
   }
+  asm volatile("" ::"v"(nr_sink));  // the next layer's router line, long since arrived
 }
 
 template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD>

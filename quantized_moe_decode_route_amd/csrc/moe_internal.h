@@ -381,7 +381,7 @@ hipError_t launch_fused_layer(int fmt, int dfmt, const float* router_w, const ui
                               const WeightRef& gate, const WeightRef& up, const WeightRef& down, int E, int D, int Fd,
                               int k, int B, uint8_t* ws, const WsLayout& L, float* y, const float* residual,
                               int32_t* idx_out, float* gw_out, uint64_t* trace, hipStream_t s,
-                              const HashRoute& hr = HashRoute{});
+                              const HashRoute& hr = HashRoute{}, const float* next_router = nullptr);
 constexpr int kFusedNormMaxD = 4096;
 
 }  // namespace moe
