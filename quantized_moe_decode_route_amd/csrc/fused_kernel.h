@@ -669,7 +669,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         if (r < k && lines > 0) {
           while (lds_get(&s_pre_n) <= r && wall_clock64() - t0 < kSpinTicks)
             __builtin_amdgcn_s_sleep(1);
-          const int e = lds_get(&s_pre[r]);
+          const int e = min(max(lds_get(&s_pre[r]), 0), E - 1);  // in bounds even after a timed-out wait
           const uint8_t* q8 = a.gate.base;
           if (p < 2 * lines) {
             const WeightRef& m = p < lines ? a.gate : a.up;
