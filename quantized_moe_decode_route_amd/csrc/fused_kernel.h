@@ -338,6 +338,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 
   const int UG = F::units(D);
   uint32_t xraw[2][F::kXRaw];
+  // MXFP4 with x given: a workgroup with a router row stages the activations
+  // from the chunks it loads for the logits (thread i holds elements
+  // 8i..8i+7 of every token, which is chunk i%4 of unit i/4 in the staged
+  // order once the bf16 halves of each dword are swapped), so they are not
+  // read a second time.
+  const bool early_x = std::is_same<F, MxFmt>::value && !NORM && D <= 8 * kW * kWave && g < E;
   // (The LDS words cleared above are next used after the logits' barriers.)
 
   // ---------------------------------------------------------------- 1. routing
@@ -424,6 +430,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
     if (g >= E) __syncthreads();  // the x chunks in LDS are read by other threads below
   } else {
+    uint4 xkeep[kMaxTok];  // this thread's x chunks of the first router row, for the staging
     for (int e = g; e < E; e += G) {
       const float* row = a.router_w + (int64_t)e * D;
       double acc[kMaxTok];
@@ -438,6 +445,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
           xall[t] = *reinterpret_cast<const uint4*>(a.x + (int64_t)min(t, B - 1) * D + c);
         take_arrival();
         dot8(acc, w0, w1, xall);
+        if (e == g) {
+#pragma unroll
+          for (int t = 0; t < kMaxTok; ++t) xkeep[t] = xall[t];
+        }
       };
       // One 8-weight chunk per thread in straight-line code when the row
       // fits (d_model <= 4096): no loop header for the compiler to wait at.
@@ -447,6 +458,21 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         for (int c = 8 * threadIdx.x; c < D; c += 8 * kW * kWave) chunk(c);
       }
       publish_logits(e, acc);
+    }
+    if constexpr (std::is_same<F, MxFmt>::value) {
+      static_assert(F::kUnitW == 32 && kCh == 4, "a thread's 8 elements are one 16-byte staged chunk");
+      if (early_x && 8 * (int)threadIdx.x < D) {  // after the logits are out: not on their path
+        const int i = threadIdx.x;
+#pragma unroll
+        for (int t = 0; t < kMaxTok; ++t) {
+          if (t < B) {
+            const uint4 v = xkeep[t];
+            reinterpret_cast<uint4*>(s_buf)[(t * kCh + i % 4) * UG + i / 4] =
+                make_uint4(__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
+                           __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16));
+          }
+        }
+      }
     }
   }
   take_arrival();  // workgroups without a router row
@@ -459,7 +485,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int i = threadIdx.x + q * kW * kWave;
-    if (i < B * UG) {
+    if (!early_x && i < B * UG) {
       if constexpr (NORM)
         F::load_x(reinterpret_cast<const uint16_t*>(s_buf) + (i / UG) * D, i - (i / UG) * UG, xraw[q]);
       else
@@ -634,7 +660,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int i = threadIdx.x + q * kW * kWave;
-    if (i < B * UG) {
+    if (!early_x && i < B * UG) {
       const int t = i / UG, u = i - (i / UG) * UG;
       uint32_t xs[F::kXDw];
       F::pack_x(xraw[q], xs);
