@@ -652,10 +652,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // above were issued after them).  They are opaque until here, so the
   // compiler cannot hoist their rearrangement into the routing, where it
   // would wait for x.
+  if (!early_x) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int i = 0; i < F::kXRaw; ++i) asm volatile("" : "+v"(xraw[q][i]));
+      for (int i = 0; i < F::kXRaw; ++i) asm volatile("" : "+v"(xraw[q][i]));
+  }
   uint4* xl = reinterpret_cast<uint4*>(s_buf);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -680,14 +682,14 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   uint32_t pre_sink[kPrefetchExperts];
 #pragma unroll
   for (int r = 0; r < kPrefetchExperts; ++r) pre_sink[r] = 0u;
-  if constexpr (std::is_same<F, MxFmt>::value) {
+  {
     if (B == 1 && w >= 1) {
       const int FSp = Fd / NX, RPWp = (FSp + GX - 1) / GX;
       const int fr = xcd * FSp + ((int)(blockIdx.x / NX) % GX) * RPWp;
       const int rows = min(RPWp, xcd * FSp + FSp - fr);
-      const int64_t rb = (int64_t)(D / 32) * 17;  // bytes per row
-      const int64_t nbytes = rows > 0 ? rows * rb : 0;
-      const int lines = (int)((nbytes + 127) / 128);
+      const int64_t rb = F::row_bytes(D), sb = F::scale_row_bytes(D);  // bytes per row: blocks or codes, scales
+      const int64_t nbytes = rows > 0 ? rows * rb : 0, sbytes = rows > 0 ? rows * sb : 0;
+      const int lines = (int)((nbytes + 127) / 128), slines = (int)((sbytes + 127) / 128);
       const int p = (int)threadIdx.x - kWave;
       const uint64_t t0 = wall_clock64();
 #pragma unroll
@@ -701,12 +703,17 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
             const WeightRef& m = p < lines ? a.gate : a.up;
             const int64_t off = min((int64_t)(p < lines ? p : p - lines) * 128, nbytes - 1);
             q8 = m.base + e * m.stride + fr * rb + off;
+          } else if (p < 2 * lines + 2 * slines) {  // INT4: the rows' scales
+            const int q = p - 2 * lines;
+            const WeightRef& m = q < slines ? a.gate : a.up;
+            const int64_t off = min((int64_t)(q < slines ? q : q - slines) * 128, sbytes - 1);
+            q8 = reinterpret_cast<const uint8_t*>(m.scale) + e * m.scale_stride + fr * sb + off;
           } else if (kPrefetchDown && DNK == 2 && a.down.layout == MOE_LAYOUT_MFMA16 && Fd / NX == 256) {
             // the expert's down blocks of this slice for the workgroup's output
             // rows: one contiguous run in the MOE_LAYOUT_MFMA16 order
             const int RPWdp = (D + GX - 1) / GX;
             const int nd0 = ((int)(blockIdx.x / NX) % GX) * RPWdp;
-            const int q = p - 2 * lines;
+            const int q = p - 2 * lines - 2 * slines;
             if (RPWdp % 16 == 0 && nd0 + RPWdp <= D && q * 128 < RPWdp * 8 * 17)
               q8 = a.down.base + e * a.down.stride + mfma16_block(nd0, xcd * 8, D) * 17 + q * 128;
           }

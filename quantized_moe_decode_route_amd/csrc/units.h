@@ -49,6 +49,9 @@ struct MxFmt {
     return Row{base + n * (int64_t)(K / 32) * 17};
   }
   static __device__ __forceinline__ int units(int K) { return K / 32; }
+  // bytes of one row of the block array and of the scale array
+  static __device__ __forceinline__ int64_t row_bytes(int K) { return (int64_t)(K / 32) * 17; }
+  static __device__ __forceinline__ int64_t scale_row_bytes(int) { return 0; }
   static __device__ __forceinline__ void load(const Row& rw, int u, Raw& raw) {
     MxRaw r;
     mx_load(rw.p, 17u * u, r);
@@ -113,6 +116,8 @@ struct Q2kFmt {
     return Row{base + n * (int64_t)(K / 256) * 84};
   }
   static __device__ __forceinline__ int units(int K) { return K / 64; }
+  static __device__ __forceinline__ int64_t row_bytes(int K) { return (int64_t)(K / 256) * 84; }
+  static __device__ __forceinline__ int64_t scale_row_bytes(int) { return 0; }
   static __device__ __forceinline__ void load(const Row& rw, int u, Raw& raw) {
     const uint8_t* blk = rw.p + 84 * (u >> 2);
     const int qq = u & 3;
@@ -262,6 +267,8 @@ struct Int4Fmt {
     return Row{reinterpret_cast<const uint32_t*>(base) + n * (int64_t)(K / 8), sc + n * (int64_t)(K / 32)};
   }
   static __device__ __forceinline__ int units(int K) { return K / 32; }
+  static __device__ __forceinline__ int64_t row_bytes(int K) { return (int64_t)K / 2; }
+  static __device__ __forceinline__ int64_t scale_row_bytes(int K) { return (int64_t)(K / 32) * 2; }
   static __device__ __forceinline__ void load(const Row& rw, int u, Raw& raw) {
     const uint4 v = *reinterpret_cast<const uint4*>(rw.q + 4 * u);
     raw.q[0] = v.x;
