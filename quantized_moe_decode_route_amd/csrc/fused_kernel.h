@@ -338,12 +338,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 
   const int UG = F::units(D);
   uint32_t xraw[2][F::kXRaw];
-  // MXFP4 with x given: a workgroup with a router row stages the activations
-  // from the chunks it loads for the logits (thread i holds elements
-  // 8i..8i+7 of every token, which is chunk i%4 of unit i/4 in the staged
-  // order once the bf16 halves of each dword are swapped), so they are not
-  // read a second time.
-  const bool early_x = std::is_same<F, MxFmt>::value && !NORM && D <= 8 * kW * kWave && g < E;
+  // With x given, a workgroup with a router row stages the activations from
+  // the chunks it loads for the logits (thread i holds elements 8i..8i+7 of
+  // every token; F::stage8 puts them in the staged order with the same bits
+  // as F::pack_x), so x is not read a second time.
+  const bool early_x = !NORM && D <= 8 * kW * kWave && g < E;
   // (The LDS words cleared above are next used after the logits' barriers.)
 
   // ---------------------------------------------------------------- 1. routing
@@ -459,20 +458,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       }
       publish_logits(e, acc);
     }
-    if constexpr (std::is_same<F, MxFmt>::value) {
-      static_assert(F::kUnitW == 32 && kCh == 4, "a thread's 8 elements are one 16-byte staged chunk");
-      if (early_x && 8 * (int)threadIdx.x < D) {  // after the logits are out: not on their path
-        const int i = threadIdx.x;
+    if (early_x && 8 * (int)threadIdx.x < D) {  // after the logits are out: not on their path
 #pragma unroll
-        for (int t = 0; t < kMaxTok; ++t) {
-          if (t < B) {
-            const uint4 v = xkeep[t];
-            reinterpret_cast<uint4*>(s_buf)[(t * kCh + i % 4) * UG + i / 4] =
-                make_uint4(__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
-                           __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16));
-          }
-        }
-      }
+      for (int t = 0; t < kMaxTok; ++t)
+        if (t < B) F::stage8(xkeep[t], threadIdx.x, reinterpret_cast<uint4*>(s_buf) + (size_t)t * kCh * UG, UG);
     }
   }
   take_arrival();  // workgroups without a router row

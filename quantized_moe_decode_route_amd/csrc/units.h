@@ -82,6 +82,14 @@ struct MxFmt {
 #pragma unroll
     for (int j = 0; j < 16; ++j) xs[j] = __builtin_amdgcn_alignbit(p[j], p[j], 16);
   }
+  // The same staging from thread i's activations 8i..8i+7 of one token (v,
+  // as loaded): chunk i%4 of unit i/4; xt is the token's staged array
+  // [kXDw/4][units].  Gives the same bits as pack_x.
+  static __device__ __forceinline__ void stage8(const uint4& v, int i, uint4* xt, int UG) {
+    xt[(i % 4) * UG + i / 4] =
+        make_uint4(__builtin_amdgcn_alignbit(v.x, v.x, 16), __builtin_amdgcn_alignbit(v.y, v.y, 16),
+                   __builtin_amdgcn_alignbit(v.z, v.z, 16), __builtin_amdgcn_alignbit(v.w, v.w, 16));
+  }
   // Code byte j holds element 2j in its high nibble and 2j+1 in its low one,
   // matching the staged pair order.
   static __device__ __forceinline__ float gu_dot(const Raw& raw, uint32_t sh, const uint32_t (&xs)[kXDw]) {
@@ -159,19 +167,39 @@ struct Q2kFmt {
 #pragma unroll
     for (int c = 0; c < kXRaw / 4; ++c) load_u4(xt + kUnitW * u + 8 * c, p + 4 * c);
   }
+  // Sum of the four activations in dwords a, b: (a0 + a1) + (b0 + b1).
+  static __device__ __forceinline__ float pair_sum(uint32_t a, uint32_t b) {
+    return (bf16_to_f32(a & 0xFFFFu) + bf16_to_f32(a >> 16)) + (bf16_to_f32(b & 0xFFFFu) + bf16_to_f32(b >> 16));
+  }
+  // A sub-block's sum is (P0 + P1) + (P2 + P3) over its four dword pairs, so
+  // that two threads holding eight activations each can form it.
   static __device__ __forceinline__ void pack_x(const uint32_t (&p)[kXRaw], uint32_t (&xs)[kXDw]) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      float sum = 0.0f;
+      float ps[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const uint32_t a = p[8 * s + 2 * c], b = p[8 * s + 2 * c + 1];
         xs[8 * s + c] = __builtin_amdgcn_perm(b, a, 0x05040100u);      // x[+0] | x[+2] << 16
         xs[8 * s + 4 + c] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // x[+1] | x[+3] << 16
-        sum += (bf16_to_f32(a & 0xFFFFu) + bf16_to_f32(a >> 16)) + (bf16_to_f32(b & 0xFFFFu) + bf16_to_f32(b >> 16));
+        ps[c] = pair_sum(a, b);
       }
-      xs[32 + s] = __float_as_uint(sum);
+      xs[32 + s] = __float_as_uint((ps[0] + ps[1]) + (ps[2] + ps[3]));
     }
+  }
+  // The same staging from thread i's activations 8i..8i+7 (v): half h = i%2
+  // of sub-block (i%8)/2 of unit i/8.  The two threads of a sub-block are
+  // adjacent lanes; their partial sums meet through a DPP swap (x + y and
+  // y + x round alike).  Gives the same bits as pack_x.
+  static __device__ __forceinline__ void stage8(const uint4& v, int i, uint4* xt, int UG) {
+    const int u = i / 8, s = (i % 8) / 2, h = i % 2;
+    reinterpret_cast<uint2*>(xt + (2 * s) * UG + u)[h] =
+        make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u));
+    reinterpret_cast<uint2*>(xt + (2 * s + 1) * UG + u)[h] =
+        make_uint2(__builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+    const float q = pair_sum(v.x, v.y) + pair_sum(v.z, v.w);
+    const float sum = q + __int_as_float(dpp_i<0xB1>(__float_as_int(q), 0));  // quad_perm [1,0,3,2]
+    if (h == 0) reinterpret_cast<uint32_t*>(xt + 8 * UG + u)[s] = __float_as_uint(sum);
   }
   // The 2-bit codes 0..3 equal twice the E2M1 values of nibbles 0..3, so each
   // code is moved into a nibble and widened by the FP4 conversion; the factor
@@ -300,19 +328,41 @@ struct Int4Fmt {
 #pragma unroll
     for (int c = 0; c < kXRaw / 4; ++c) load_u4(xt + kUnitW * u + 8 * c, p + 4 * c);
   }
+  // Sum of the eight activations of one code word, dword by dword.
+  static __device__ __forceinline__ float word_sum(uint32_t p0, uint32_t p1, uint32_t p2, uint32_t p3) {
+    float c = bf16_to_f32(p0 & 0xFFFFu) + bf16_to_f32(p0 >> 16);
+    c += bf16_to_f32(p1 & 0xFFFFu) + bf16_to_f32(p1 >> 16);
+    c += bf16_to_f32(p2 & 0xFFFFu) + bf16_to_f32(p2 >> 16);
+    c += bf16_to_f32(p3 & 0xFFFFu) + bf16_to_f32(p3 >> 16);
+    return c;
+  }
+  // The unit's sum is (c0 + c1) + (c2 + c3) over its four code words, so
+  // that four threads holding eight activations each can form it.
   static __device__ __forceinline__ void pack_x(const uint32_t (&p)[kXRaw], uint32_t (&xs)[kXDw]) {
-    float sum = 0.0f;
+    float c[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       xs[4 * w + 0] = __builtin_amdgcn_perm(p[4 * w + 1], p[4 * w + 0], 0x05040100u);  // x0 | x2 << 16
       xs[4 * w + 1] = __builtin_amdgcn_perm(p[4 * w + 3], p[4 * w + 2], 0x05040100u);  // x4 | x6 << 16
       xs[4 * w + 2] = __builtin_amdgcn_perm(p[4 * w + 1], p[4 * w + 0], 0x07060302u);  // x1 | x3 << 16
       xs[4 * w + 3] = __builtin_amdgcn_perm(p[4 * w + 3], p[4 * w + 2], 0x07060302u);  // x5 | x7 << 16
-#pragma unroll
-      for (int m = 0; m < 4; ++m) sum += bf16_to_f32(p[4 * w + m] & 0xFFFFu) + bf16_to_f32(p[4 * w + m] >> 16);
+      c[w] = word_sum(p[4 * w], p[4 * w + 1], p[4 * w + 2], p[4 * w + 3]);
     }
-    xs[16] = __float_as_uint(sum);
+    xs[16] = __float_as_uint((c[0] + c[1]) + (c[2] + c[3]));
     xs[17] = xs[18] = xs[19] = 0u;
+  }
+  // The same staging from thread i's activations 8i..8i+7 (v): code word
+  // i%4 of unit i/4.  The four threads of a unit are one lane quad; their
+  // word sums meet through two DPP swaps (x + y and y + x round alike).
+  // Gives the same bits as pack_x.
+  static __device__ __forceinline__ void stage8(const uint4& v, int i, uint4* xt, int UG) {
+    const int u = i / 4, w = i % 4;
+    xt[w * UG + u] = make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x05040100u),
+                                __builtin_amdgcn_perm(v.y, v.x, 0x07060302u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+    float c = word_sum(v.x, v.y, v.z, v.w);
+    c += __int_as_float(dpp_i<0xB1>(__float_as_int(c), 0));  // quad_perm [1,0,3,2]: c0 + c1, c2 + c3
+    c += __int_as_float(dpp_i<0x4E>(__float_as_int(c), 0));  // quad_perm [2,3,0,1]
+    if (w == 0) xt[4 * UG + u] = make_uint4(__float_as_uint(c), 0u, 0u, 0u);
   }
   static __device__ __forceinline__ float gu_dot(const Raw& raw, uint32_t, const uint32_t (&xs)[kXDw]) {
     float acc = 0.0f;  // sum of u * 2^-9 * x
