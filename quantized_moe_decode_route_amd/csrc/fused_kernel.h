@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // the chunks it loads for the logits (thread i holds elements 8i..8i+7 of
   // every token; F::stage8 puts them in the staged order with the same bits
   // as F::pack_x), so x is not read a second time.
-  const bool early_x = !NORM && D <= 8 * kW * kWave && g < E;
+  const bool early_x = NORM || (D <= 8 * kW * kWave && g < E);
   // (The LDS words cleared above are next used after the logits' barriers.)
 
   // ---------------------------------------------------------------- 1. routing
@@ -391,8 +391,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     // One token (B = 1): its activations are the RMS-normalised residual
     // stream, computed here in the chunk order of rms_total (thread i:
     // elements 8i..8i+7, d_model <= 4096) while the first router row is on
-    // its way.  Each thread keeps its chunk for the logits and leaves it in
-    // LDS (s_buf as x [D], until the activations are staged) for gate/up.
+    // its way.  Each thread keeps its chunk for the logits and stages it in
+    // LDS for gate/up (F::stage8).
     // The loads are issued unconditionally (clamped to valid rows), h first:
     // the norm then waits for h alone while the router row is in flight.
     const bool mine = 8 * (int)threadIdx.x < D;
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     bool near = !sc.fast;
     uint4 xn = rms_x8_fast(ha, hb, sc.r, near);
     if (near) xn = rms_x8_exact(ha, hb, sc.denom);  // rare: the exact quotients
-    if (mine) reinterpret_cast<uint4*>(s_buf)[threadIdx.x] = xn;
+    if (mine) F::stage8(xn, threadIdx.x, reinterpret_cast<uint4*>(s_buf), UG);
     uint4 xall[kMaxTok];
 #pragma unroll
     for (int t = 0; t < kMaxTok; ++t) xall[t] = xn;
@@ -427,7 +427,6 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       if (mine) dot8(acc, w0, w1, xall);
       publish_logits(e, acc);
     }
-    if (g >= E) __syncthreads();  // the x chunks in LDS are read by other threads below
   } else {
     uint4 xkeep[kMaxTok];  // this thread's x chunks of the first router row, for the staging
     for (int e = g; e < E; e += G) {
@@ -475,10 +474,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   for (int q = 0; q < 2; ++q) {
     const int i = threadIdx.x + q * kW * kWave;
     if (!early_x && i < B * UG) {
-      if constexpr (NORM)
-        F::load_x(reinterpret_cast<const uint16_t*>(s_buf) + (i / UG) * D, i - (i / UG) * UG, xraw[q]);
-      else
-        F::load_x(a.x + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);
+      F::load_x(a.x + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);  // (never with NORM: staged above)
     }
   }
   stamp(a, 2);
