@@ -421,7 +421,11 @@ def main():
     log("per-kernel event timing ...")
     k1 = profile_kernel(layers, x1, 1, args.steps, args.warmup, ws)
     k8 = profile_kernel(layers, x8, 8, args.steps, args.warmup, ws)
-    achieved = bytes1 / (k1 * 1e-3) / 1e9
+    # One layer launch per step: the average launch duration is the timed
+    # region's HIP-event time on the launch stream divided by the launches.
+    # (Events around each launch add their own marker overhead; reported as
+    # launch_bracket_ms.)
+    achieved = bytes1 / (ms1 * 1e-3) / 1e9
 
     result = {
         "metric": METRIC,
@@ -447,11 +451,11 @@ def main():
                "pct_hbm_peak": round(100 * gbs8 / HBM_PEAK_GBS, 2),
                "tokens_per_s_layer": round(8e3 / ms8, 1), "mean_unique_experts": round(U8, 2),
                "bytes_per_step": round(bytes8)},
-        "kernel_ms": {"b1": round(k1, 5), "b8": round(k8, 5)},
+        "launch_bracket_ms": {"b1": round(k1, 5), "b8": round(k8, 5)},
         "roofline": {"kernel": "fused_layer_kernel (MXFP4, B=1)", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(), "bytes_per_launch": bytes1,
-                     "b8_achieved": round(bytes8 / (k8 * 1e-3) / 1e9, 2)},
+                     "traffic": measured_traffic(), "bytes_per_launch": bytes1, "launch_ms": round(ms1, 5),
+                     "b8_achieved": round(gbs8, 2)},
     }
     if not args.no_extra:
         del layers
