@@ -466,10 +466,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   take_arrival();  // workgroups without a router row
   if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints] = t_start;
   stamp(a, 1);
-  // Activations for gate/up: requested now that the router weights are in,
-  // staged in LDS ([t][chunk][unit], so lanes read consecutive chunks) after
-  // the routing, which hides their latency.  B * units <= 2 * blockDim for
-  // every shape this kernel accepts.
+  // Activations for gate/up of a workgroup that has not staged them above
+  // (no router row): requested now, staged in LDS ([t][chunk][unit], so
+  // lanes read consecutive chunks) after the routing, which hides their
+  // latency.  B * units <= 2 * blockDim for every shape this kernel accepts.
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int i = threadIdx.x + q * kW * kWave;
@@ -633,9 +633,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       a.trace[blockIdx.x * kTracePoints + kTracePoints - 1] = (uint64_t)xcd_arrival;
     }
   }
-  // Stage the activations (their loads have long returned: the logit reads
-  // above were issued after them).  They are opaque until here, so the
-  // compiler cannot hoist their rearrangement into the routing, where it
+  // Stage the activations requested above (their loads have long returned:
+  // the logit reads were issued after them).  They are opaque until here, so
+  // the compiler cannot hoist their rearrangement into the routing, where it
   // would wait for x.
   if (!early_x) {
 #pragma unroll
