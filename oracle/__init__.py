@@ -103,6 +103,15 @@ def lib():
         L.oracle_quantize_fp4_to_int4g32.restype = ctypes.c_int
         L.oracle_quantize_fp4_to_int4g32.argtypes = [_u8p, ctypes.c_int64, _i32p, _u16p,
                                                      ctypes.c_void_p, ctypes.c_void_p]
+        _i8p = np.ctypeslib.ndpointer(dtype=np.int8, flags="C_CONTIGUOUS")
+        L.oracle_q8k_quantize.restype = ctypes.c_int
+        L.oracle_q8k_quantize.argtypes = [_fp, ctypes.c_int, ctypes.c_int, _i8p, _fp]
+        L.oracle_gemv_mxfp4_q8.restype = ctypes.c_int
+        L.oracle_gemv_mxfp4_q8.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, _i8p, _fp, ctypes.c_int, _dp, _dp]
+        L.oracle_mxfp4_half_lut.restype = None
+        L.oracle_mxfp4_half_lut.argtypes = [_u16p]
+        L.oracle_gemv_mxfp4_half.restype = ctypes.c_int
+        L.oracle_gemv_mxfp4_half.argtypes = [_u8p, ctypes.c_int, ctypes.c_int, _dp, ctypes.c_int, _dp]
         _LIB = L
     return _LIB
 
@@ -374,3 +383,49 @@ def quantize_fp4_to_int4g32(mx: np.ndarray, n_rows: int, k: int, with_detail: bo
     if with_detail:
         return q, s, s_f.reshape(n_rows, k // 32), r_i.reshape(n_rows, k // 32)
     return q, s
+
+
+# ---------------------------------------------------------------- alternative numerics
+# ("ds4.c study notes", glossary page "quantization": "MXFP4's ROCm native
+# kernel" -- Q8_K activations with integer dot products; "Metal's MXFP4 ->
+# half lookup table" -- exactly rounded binary16 products of scale and code.)
+
+def q8k_quantize(x: np.ndarray):
+    """fp32 activations [B, K] (K % 256 == 0) -> (q int8 [B, K], d fp32 [B, K/256]):
+    per 256 activations d = fp32(max|x| / 127), q = clamp(rint(x / d), +-127) in fp32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    B, K = x.shape
+    q = np.empty((B, K), dtype=np.int8)
+    d = np.empty((B, K // 256), dtype=np.float32)
+    _check(lib().oracle_q8k_quantize(x.reshape(-1), B, K, q.reshape(-1), d.reshape(-1)), "q8k_quantize")
+    return q, d
+
+
+def gemv_mxfp4_q8(blocks, n_rows: int, k: int, q: np.ndarray, d: np.ndarray):
+    """MXFP4 weights [n_rows, k] against Q8 activations: (y fp64 [B, n_rows], sum of |block terms|)."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    d = np.ascontiguousarray(d, dtype=np.float32)
+    B = q.shape[0]
+    y = np.empty((B, n_rows), dtype=np.float64)
+    a = np.empty((B, n_rows), dtype=np.float64)
+    _check(lib().oracle_gemv_mxfp4_q8(b, n_rows, k, q.reshape(-1), d.reshape(-1), B, y.reshape(-1), a.reshape(-1)),
+           "gemv_mxfp4_q8")
+    return y, a
+
+
+def mxfp4_half_lut() -> np.ndarray:
+    """uint16 [256, 16]: binary16 bits of E2M1(c) * 2^(e - 127), one round-to-nearest-even."""
+    out = np.empty(256 * 16, dtype=np.uint16)
+    lib().oracle_mxfp4_half_lut(out)
+    return out.reshape(256, 16)
+
+
+def gemv_mxfp4_half(blocks, n_rows: int, k: int, x: np.ndarray) -> np.ndarray:
+    """y = W x in fp64 with W decoded through ``mxfp4_half_lut``."""
+    b = np.ascontiguousarray(blocks, dtype=np.uint8).reshape(-1)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    B = x.shape[0]
+    y = np.empty((B, n_rows), dtype=np.float64)
+    _check(lib().oracle_gemv_mxfp4_half(b, n_rows, k, x.reshape(-1), B, y.reshape(-1)), "gemv_mxfp4_half")
+    return y

@@ -26,6 +26,9 @@
  *  [mixed]  "Mixed-precision compression of DeepSeek-V4-Flash": "The recipe"
  *           (256 routed experts, top-6 kept), "What compression does not
  *           solve" (decode streams the active weights).
+ *  [ds4-q] also: "Metal's MXFP4 -> half lookup table" (the 256 x 16 table of
+ *           exactly rounded binary16 products) and "MXFP4's ROCm native
+ *           kernel" (activations quantized to Q8_K, integer dot products).
  *
  * Parity unpinned: none of the functions below lacks a pin, except that the
  * composition of 43 stacked layers is checked only layer by layer.
@@ -494,5 +497,123 @@ int oracle_quantize_fp4_to_int4g32(const uint8_t* mx, int64_t ngroups, int32_t* 
     if (s_out) s_out[g] = best_s;
     if (r_out) r_out[g] = best_j;
   }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------ alternative numerics
+ * [ds4-q] "MXFP4's ROCm native kernel": the activations are quantized to
+ * Q8_K on the GPU and the weights' codes are dotted with them as integers.
+ * The pages name Q8_K but do not define it; the reading used here: for every
+ * 256 consecutive activations of a token, d = fp32(max|x| / 127) and
+ * q = clamp(rint(x / d), -127, 127), both in fp32 (IEEE division, ties to
+ * even); a block of zeros has d = 0 and q = 0.
+ */
+int oracle_q8k_quantize(const float* x, int B, int K, int8_t* q, float* d) {
+  if (!x || !q || !d || B < 1 || K < 256 || K % 256) return ORACLE_ERR_ARG;
+  for (int t = 0; t < B; ++t) {
+    for (int b = 0; b < K / 256; ++b) {
+      const float* xb = x + (int64_t)t * K + 256 * b;
+      float amax = 0.0f;
+      for (int i = 0; i < 256; ++i) {
+        const float a = fabsf(xb[i]);
+        if (a > amax) amax = a;
+      }
+      const float db = amax / 127.0f;
+      d[(int64_t)t * (K / 256) + b] = db;
+      for (int i = 0; i < 256; ++i) {
+        float r = db > 0.0f ? rintf(xb[i] / db) : 0.0f;
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        q[(int64_t)t * K + 256 * b + i] = (int8_t)r;
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* y[t][n] = sum over blocks j of 2^(e - 127) * d[t][j / 8] * sum_i E2M1(c_i) *
+ * q[t][32 j + i]: the MXFP4 weights against the Q8 activations.  Twice an
+ * E2M1 value is an integer (0..12), so the inner sum is an exact integer and
+ * every block term is exact in fp64; terms are added in block order.
+ * absy[t][n] receives the sum of the terms' magnitudes (for error bounds). */
+int oracle_gemv_mxfp4_q8(const uint8_t* blocks, int N, int K, const int8_t* q, const float* d, int B, double* y,
+                         double* absy) {
+  if (!blocks || !q || !d || !y || N < 1 || K < 256 || K % 256 || B < 1) return ORACLE_ERR_ARG;
+  for (int t = 0; t < B; ++t) {
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0, aacc = 0.0;
+      for (int j = 0; j < K / 32; ++j) {
+        const uint8_t* blk = blocks + ((int64_t)n * (K / 32) + j) * 17;
+        long isum = 0;
+        for (int i = 0; i < 32; ++i) {
+          const int code = (i % 2 == 0) ? (blk[1 + i / 2] >> 4) : (blk[1 + i / 2] & 0xF);
+          const long c2 = (long)(2.0 * oracle_e2m1(code));
+          isum += c2 * (long)q[(int64_t)t * K + 32 * j + i];
+        }
+        const double term = (double)isum * ldexp(1.0, (int)blk[0] - 128) * (double)d[(int64_t)t * (K / 256) + j / 8];
+        acc += term;
+        aacc += fabs(term);
+      }
+      y[(int64_t)t * N + n] = acc;
+      if (absy) absy[(int64_t)t * N + n] = aacc;
+    }
+  }
+  return ORACLE_OK;
+}
+
+/* [ds4-q] "Metal's MXFP4 -> half lookup table": entry [e][c] is the binary16
+ * pattern of E2M1(c) * 2^(e - 127), rounded once to nearest-even with exact
+ * integer arithmetic.  The pages keep an arithmetic path for e = 255 (an
+ * infinite scale); reading: that row holds the quiet NaN 0x7E00. */
+static uint16_t half_of_scaled_code(int e, int code) {
+  const uint16_t sign = (code & 8) ? 0x8000 : 0;
+  const int m = (int)(2.0 * fabs(oracle_e2m1(code)));  /* |value| = m * 2^(e - 128), m in 0..12 */
+  if (m == 0) return sign;
+  const int k = e - 128;
+  int L = 0;  /* bit length of m */
+  while ((m >> L) != 0) ++L;
+  const int E = k + L - 1;  /* |value| = 1.f * 2^E */
+  if (E > 15) return sign | 0x7C00;  /* overflow: m has at most 4 significant bits, so no rounding reaches it */
+  if (E >= -14) {
+    /* normal: 10 fraction bits hold m's L - 1 fraction bits exactly */
+    const int frac = (m << (10 - (L - 1))) & 0x3FF;
+    return sign | (uint16_t)(((E + 15) << 10) | frac);
+  }
+  /* subnormal: count of 2^-24 units = m * 2^(k + 24), rounded to nearest-even */
+  const int s = k + 24;
+  if (s >= 0) return sign | (uint16_t)(m << s);
+  const int sh = -s;
+  if (sh > 6) return sign; /* m * 2^-sh < 12/128 < 1/2: rounds to zero */
+  const int whole = m >> sh, rem = m & ((1 << sh) - 1), half = 1 << (sh - 1);
+  int r = whole;
+  if (rem > half || (rem == half && (whole & 1))) ++r;
+  return sign | (uint16_t)r;
+}
+
+void oracle_mxfp4_half_lut(uint16_t* out) {
+  for (int e = 0; e < 256; ++e)
+    for (int c = 0; c < 16; ++c) out[e * 16 + c] = e == 255 ? 0x7E00 : half_of_scaled_code(e, c);
+}
+
+/* y[t][n] = sum_k half(W[n][k]) * x[t][k] in fp64, the weights decoded
+ * through the table above (k ascending). */
+int oracle_gemv_mxfp4_half(const uint8_t* blocks, int N, int K, const double* x, int B, double* y) {
+  if (!blocks || !x || !y || N < 1 || K < 32 || K % 32 || B < 1) return ORACLE_ERR_ARG;
+  uint16_t* lut = (uint16_t*)malloc(256 * 16 * sizeof(uint16_t));
+  if (!lut) return ORACLE_ERR_ARG;
+  oracle_mxfp4_half_lut(lut);
+  for (int t = 0; t < B; ++t) {
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) {
+        const uint8_t* blk = blocks + ((int64_t)n * (K / 32) + k / 32) * 17;
+        const int i = k % 32;
+        const int code = (i % 2 == 0) ? (blk[1 + i / 2] >> 4) : (blk[1 + i / 2] & 0xF);
+        acc += oracle_f16_to_double(lut[blk[0] * 16 + code]) * x[(int64_t)t * K + k];
+      }
+      y[(int64_t)t * N + n] = acc;
+    }
+  }
+  free(lut);
   return ORACLE_OK;
 }

@@ -629,3 +629,103 @@ def test_hashed_layer_composition():
                                         hashed=(table, np.array([0], dtype=np.int32)))
     y_l, i_l, g_l = oracle.layer_decode("mxfp4", lambda e: experts[e], wr, xb, k, F)
     assert np.array_equal(i_h, i_l) and np.array_equal(g_h, g_l) and np.array_equal(y_h, y_l)
+
+
+# ---------------------------------------------------------------- alternative numerics
+# "ds4.c study notes", glossary page "quantization": "MXFP4's ROCm native
+# kernel" (Q8_K activations, integer dots) and "Metal's MXFP4 -> half lookup
+# table" (exactly rounded binary16 products).
+
+def test_q8k_quantize_closed_forms():
+    k = np.arange(-127, 128)
+    x = np.concatenate([k * 0.5, [0.0]]).astype(np.float32).reshape(1, 256)  # max |x| = 63.5: d = 0.5 exactly
+    q, d = oracle.q8k_quantize(x)
+    assert d[0, 0] == np.float32(0.5)
+    assert np.array_equal(q[0, :255], k) and q[0, 255] == 0
+    x = np.zeros((1, 256), np.float32)
+    x[0, :4] = [127.0, 2.5, 3.5, -2.5]  # d = 1: ties go to the even integer
+    q, d = oracle.q8k_quantize(x)
+    assert d[0, 0] == 1.0 and list(q[0, :4]) == [127, 2, 4, -2]
+    x = np.zeros((2, 512), np.float32)
+    x[1, 300] = -5.0
+    q, d = oracle.q8k_quantize(x)
+    assert np.all(d[0] == 0) and np.all(q[0] == 0) and d[1, 0] == 0  # a block of zeros: d = 0, q = 0
+    assert d[1, 1] == np.float32(5.0) / np.float32(127.0) and q[1, 300] == -127
+
+
+def test_q8k_quantize_error_bound():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((3, 1024)) * np.exp(rng.uniform(-4, 4, size=(3, 1)))).astype(np.float32)
+    q, d = oracle.q8k_quantize(x)
+    dd = np.repeat(d.astype(np.float64), 256, axis=1)
+    assert np.all(np.abs(q.astype(np.int32)) <= 127)
+    assert np.all(np.abs(x.astype(np.float64) - dd * q) <= dd * (0.5 + 127 * 2.0 ** -23))
+    assert np.all(np.abs(q).reshape(3, 4, 256).max(axis=2) == 127)  # each block's largest value maps to +-127
+
+
+def test_gemv_mxfp4_q8_integer_route_matches_float_route():
+    rng = np.random.default_rng(12)
+    N, K = 24, 768
+    blocks = _rand_mx(N, K, rng)
+    x = rng.standard_normal((3, K)).astype(np.float32)
+    q, d = oracle.q8k_quantize(x)
+    y, a = oracle.gemv_mxfp4_q8(blocks, N, K, q, d)
+    xd = q.astype(np.float64) * np.repeat(d.astype(np.float64), 256, axis=1)  # exact
+    y2 = oracle.gemv("mxfp4", blocks, N, K, xd)
+    assert np.all(np.abs(y - y2) <= 1e-13 * a)
+
+
+def test_gemv_mxfp4_q8_handbuilt():
+    # scale byte 128 (x2) and code 1 (0.5): every weight is 1; q = 1 with d = 0.25 -> y = K / 4
+    K = 512
+    blocks = np.concatenate([mx_block(128, [1] * 32) for _ in range(K // 32)])
+    q = np.ones((1, K), np.int8)
+    d = np.full((1, K // 256), 0.25, np.float32)
+    y, a = oracle.gemv_mxfp4_q8(blocks, 1, K, q, d)
+    assert y[0, 0] == K / 4 and a[0, 0] == K / 4
+    # code 15 (-6) in the high nibble of byte 0 only: element 0, the first activation
+    codes = [0] * 32
+    codes[0] = 15
+    blocks = np.concatenate([mx_block(127, codes)] + [mx_block(127, [0] * 32) for _ in range(K // 32 - 1)])
+    q = np.zeros((1, K), np.int8)
+    q[0, 0], q[0, 1] = 3, 100
+    y, _ = oracle.gemv_mxfp4_q8(blocks, 1, K, q, np.full((1, K // 256), 1.0, np.float32))
+    assert y[0, 0] == -18.0
+
+
+def test_mxfp4_half_lut_matches_independent_rounding():
+    lut = oracle.mxfp4_half_lut()
+    for e in range(255):
+        exact = np.array([oracle.e2m1(c) * 2.0 ** (e - 127) for c in range(16)], dtype=np.float64)
+        with np.errstate(over="ignore"):
+            ref = exact.astype(np.float16).view(np.uint16)  # numpy's binary64 -> binary16, ties to even
+        assert np.array_equal(lut[e], ref), e
+    assert np.all(lut[255] == 0x7E00)
+    row = np.array([oracle.e2m1(c) for c in range(16)], dtype=np.float16).view(np.uint16)
+    assert np.array_equal(lut[127], row)  # scale 1: the E2M1 table itself
+
+
+def test_mxfp4_half_lut_golden():
+    import hashlib
+    rows = read_golden("mxfp4_half_lut.txt")
+    lut = oracle.mxfp4_half_lut()
+    sha = [r[1] for r in rows if r[0] == "sha256"][0]
+    assert hashlib.sha256(lut.astype("<u2").tobytes()).hexdigest() == sha
+    for r in rows:
+        if r[0] == "entry":
+            assert lut[int(r[1]), int(r[2])] == int(r[3], 16), r
+
+
+def test_gemv_mxfp4_half_equals_exact_decode_in_range():
+    # scale bytes 118..134 keep every product a normal binary16: the table
+    # decode is then exact and the matvec equals the plain one
+    rng = np.random.default_rng(13)
+    N, K = 16, 256
+    blocks = _rand_mx(N, K, rng)
+    x = rng.standard_normal((2, K))
+    assert np.array_equal(oracle.gemv_mxfp4_half(blocks, N, K, x), oracle.gemv("mxfp4", blocks, N, K, x))
+    # out of range: scale byte 150 turns every nonzero weight into an infinity
+    big = blocks.copy().reshape(-1, 17)
+    big[:, 0] = 150
+    y = oracle.gemv_mxfp4_half(big.reshape(-1), N, K, np.abs(x) + 1.0)
+    assert np.all(np.isinf(y) | np.isnan(y))
