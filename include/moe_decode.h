@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 enum moe_status {
   MOE_OK = 0,
@@ -112,6 +112,43 @@ int moe_expert_gemv_q2k(const uint8_t* blocks /* [N][K/256][84] */, int N, int K
                         const float* x, int B, float* y, void* stream);
 int moe_expert_gemv_int4g32(const int32_t* q /* [N][K/8] */, const uint16_t* scale_bf16 /* [N][K/32] */,
                             int N, int K, const float* x, int B, float* y, void* stream);
+
+/* ------------------------------------------------------------------ alternative numerics
+ * Two other ways to form the MXFP4 matvec, kept to compare numerics and
+ * VALU cost with the matvec above ("ds4.c study notes", glossary page
+ * "quantization").
+ *
+ * "MXFP4's ROCm native kernel" quantizes the activations to Q8_K and dots
+ * the weights' codes with them as integers.  The pages name Q8_K without
+ * defining it; here, per 256 consecutive activations of a token,
+ * d = fp32(max|x| / 127) and q = clamp(rint(x / d), -127, 127) computed in
+ * fp32 (IEEE division, ties to even; a block of zeros gives d = 0, q = 0).
+ *   moe_q8k_quantize: x fp32 [B][K] (finite, 4-byte aligned), K % 256 == 0,
+ *   B >= 1 -> q int8 [B][K], d fp32 [B][K/256] (4-byte aligned).
+ *   moe_expert_gemv_mxfp4_q8: y[b][n] = sum over blocks j of
+ *   2^(e_nj - 127) * d[b][j/8] * sum_i E2M1(c_nji) * q[b][32j+i]; the inner
+ *   sums are exact integers (v_dot4 on doubled codes), scaled and summed in
+ *   fp32.  blocks as for moe_expert_gemv_mxfp4, q 16-byte aligned,
+ *   1 <= B <= MOE_MAX_TOKENS, K % 256 == 0.
+ *
+ * "Metal's MXFP4 -> half lookup table" decodes every weight with one
+ * indexed load from a 256 x 16 table: entry [e][c] is the binary16 pattern
+ * of E2M1(c) * 2^(e - 127) rounded once to nearest-even (row 255, an
+ * infinite scale, holds the quiet NaN 0x7E00).  Products outside binary16's
+ * range become infinities or round towards zero.
+ *   moe_mxfp4_half_lut: writes the table (uint16 [256][16], device memory,
+ *   2-byte aligned) as the kernels build it.
+ *   moe_expert_gemv_mxfp4_hlut: y = W x with W decoded through the table
+ *   (held in LDS), fp32 accumulation; arguments as moe_expert_gemv_mxfp4.
+ * All four are asynchronous on `stream` and return MOE_ERR_ARG / _SHAPE /
+ * _ALIGN / _ARCH before launching anything.
+ */
+int moe_q8k_quantize(const float* x, int B, int K, int8_t* q, float* d, void* stream);
+int moe_expert_gemv_mxfp4_q8(const uint8_t* blocks /* [N][K/32][17] */, int N, int K, const int8_t* q,
+                             const float* d, int B, float* y, void* stream);
+int moe_mxfp4_half_lut(uint16_t* lut /* [256][16] */, void* stream);
+int moe_expert_gemv_mxfp4_hlut(const uint8_t* blocks /* [N][K/32][17] */, int N, int K, const float* x, int B,
+                               float* y, void* stream);
 
 /* ------------------------------------------------------------------ routing
  * logits[b][e] = sum_k router_w[e][k] * x[b][k] accumulated in fp64; each

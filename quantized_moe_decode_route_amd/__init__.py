@@ -20,7 +20,7 @@ FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2k": MOE_FMT_Q2K, "int4g32": MOE_FMT_INT4G3
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE256, MOE_LAYOUT_MFMA16 = 0, 1, 2
 LAYOUTS = {"rows": MOE_LAYOUT_ROWS, "tile256": MOE_LAYOUT_TILE256, "mfma16": MOE_LAYOUT_MFMA16}
 # MOE_ABI_VERSION of include/moe_decode.h that this binding is written for
-ABI_VERSION = 5
+ABI_VERSION = 6
 MOE_MAX_TOKENS = 8
 MOE_MAX_TOPK = 8
 
@@ -32,6 +32,7 @@ EXPORTS = (
     "moe_workspace_flags", "moe_layer_decode_profiled", "moe_layer_decode_traced",
     "moe_stack_workspace_bytes", "moe_stack_decode", "moe_stack_decode_ids", "moe_rmsnorm_bf16",
     "quantize_fp4_to_int4g32", "moe_validate_mxfp4", "moe_tile_weights", "moe_tile_weights_mfma16",
+    "moe_q8k_quantize", "moe_expert_gemv_mxfp4_q8", "moe_mxfp4_half_lut", "moe_expert_gemv_mxfp4_hlut",
 )
 
 
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
             "moe_expert_gemv_mxfp4": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp]),
             "moe_expert_gemv_q2k": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp]),
             "moe_expert_gemv_int4g32": (_i, [_vp, _vp, _i, _i, _vp, _i, _vp, _vp]),
+            "moe_q8k_quantize": (_i, [_vp, _i, _i, _vp, _vp, _vp]),
+            "moe_expert_gemv_mxfp4_q8": (_i, [_vp, _i, _i, _vp, _vp, _i, _vp, _vp]),
+            "moe_mxfp4_half_lut": (_i, [_vp, _vp]),
+            "moe_expert_gemv_mxfp4_hlut": (_i, [_vp, _i, _i, _vp, _i, _vp, _vp]),
             "moe_route_workspace_bytes": (_sz, [_i, _i, _i, _i]),
             "moe_route_topk": (_i, [_vp, _i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
             "moe_layer_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
@@ -150,6 +155,27 @@ def moe_expert_gemv_mxfp4(blocks, N: int, K: int, x, y, stream=None) -> None:
     B = x.shape[0]
     _check("moe_expert_gemv_mxfp4",
            lib().moe_expert_gemv_mxfp4(_ptr(blocks), N, K, _ptr(x), B, _ptr(y), _stream(stream)))
+
+
+def moe_q8k_quantize(x, q, d, stream=None) -> None:
+    B, K = x.shape
+    _check("moe_q8k_quantize", lib().moe_q8k_quantize(_ptr(x), B, K, _ptr(q), _ptr(d), _stream(stream)))
+
+
+def moe_expert_gemv_mxfp4_q8(blocks, N: int, K: int, q, d, y, stream=None) -> None:
+    B = q.shape[0]
+    _check("moe_expert_gemv_mxfp4_q8",
+           lib().moe_expert_gemv_mxfp4_q8(_ptr(blocks), N, K, _ptr(q), _ptr(d), B, _ptr(y), _stream(stream)))
+
+
+def moe_mxfp4_half_lut(lut, stream=None) -> None:
+    _check("moe_mxfp4_half_lut", lib().moe_mxfp4_half_lut(_ptr(lut), _stream(stream)))
+
+
+def moe_expert_gemv_mxfp4_hlut(blocks, N: int, K: int, x, y, stream=None) -> None:
+    B = x.shape[0]
+    _check("moe_expert_gemv_mxfp4_hlut",
+           lib().moe_expert_gemv_mxfp4_hlut(_ptr(blocks), N, K, _ptr(x), B, _ptr(y), _stream(stream)))
 
 
 def moe_expert_gemv_q2k(blocks, N: int, K: int, x, y, stream=None) -> None:

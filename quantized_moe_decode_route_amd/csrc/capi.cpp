@@ -222,6 +222,41 @@ int moe_expert_gemv_int4g32(const int32_t* q, const uint16_t* scale_bf16, int N,
   return hip_status(launch_gemv(MOE_FMT_INT4G32, q, scale_bf16, N, K, x, B, y, (hipStream_t)stream));
 }
 
+int moe_q8k_quantize(const float* x, int B, int K, int8_t* q, float* d, void* stream) {
+  if (!x || !q || !d) return MOE_ERR_ARG;
+  if (B < 1 || K < 256 || K % 256 != 0) return MOE_ERR_SHAPE;
+  if (!aligned(x, 4) || !aligned(d, 4)) return MOE_ERR_ALIGN;
+  int st = arch_check();
+  if (st != MOE_OK) return st;
+  return hip_status(launch_q8k_quantize(x, B, K, q, d, (hipStream_t)stream));
+}
+
+int moe_expert_gemv_mxfp4_q8(const uint8_t* blocks, int N, int K, const int8_t* q, const float* d, int B, float* y,
+                             void* stream) {
+  if (!blocks || !q || !d || !y) return MOE_ERR_ARG;
+  if (N <= 0 || K <= 0) return MOE_ERR_ARG;
+  if (B < 1 || B > MOE_MAX_TOKENS || K % 256 != 0) return MOE_ERR_SHAPE;
+  if (!aligned(blocks, 4) || !aligned(q, 16) || !aligned(d, 4) || !aligned(y, 4)) return MOE_ERR_ALIGN;
+  int st = arch_check();
+  if (st != MOE_OK) return st;
+  return hip_status(launch_gemv_q8(blocks, N, K, q, d, B, y, (hipStream_t)stream));
+}
+
+int moe_mxfp4_half_lut(uint16_t* lut, void* stream) {
+  if (!lut) return MOE_ERR_ARG;
+  if (!aligned(lut, 2)) return MOE_ERR_ALIGN;
+  int st = arch_check();
+  if (st != MOE_OK) return st;
+  return hip_status(launch_half_lut(lut, (hipStream_t)stream));
+}
+
+int moe_expert_gemv_mxfp4_hlut(const uint8_t* blocks, int N, int K, const float* x, int B, float* y, void* stream) {
+  int st = check_gemv(blocks, N, K, x, B, y, MOE_FMT_MXFP4);
+  if (st != MOE_OK) return st;
+  if ((st = arch_check()) != MOE_OK) return st;
+  return hip_status(launch_gemv_hlut(blocks, N, K, x, B, y, (hipStream_t)stream));
+}
+
 size_t moe_route_workspace_bytes(int B, int D, int E, int top_k) {
   if (B < 1 || D < 1 || E < 1 || top_k < 1) return 0;
   // Routing uses the leading regions of a layer workspace, up to the

@@ -384,4 +384,11 @@ hipError_t launch_fused_layer(int fmt, int dfmt, const float* router_w, const ui
                               const HashRoute& hr = HashRoute{}, const float* next_router = nullptr);
 constexpr int kFusedNormMaxD = 4096;
 
+// Alternative numerics for the MXFP4 matvec (altnum.hip).
+hipError_t launch_q8k_quantize(const float* x, int B, int K, int8_t* q, float* d, hipStream_t s);
+hipError_t launch_gemv_q8(const uint8_t* w, int N, int K, const int8_t* q, const float* d, int B, float* y,
+                          hipStream_t s);
+hipError_t launch_half_lut(uint16_t* out, hipStream_t s);
+hipError_t launch_gemv_hlut(const uint8_t* w, int N, int K, const float* x, int B, float* y, hipStream_t s);
+
 }  // namespace moe

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert moe.moe_abi_version() == moe.ABI_VERSION == 5
+    assert moe.moe_abi_version() == moe.ABI_VERSION == 6
     for st in range(7):
         assert moe.moe_status_string(st)
     assert moe.moe_status_string(0) == "ok"
@@ -76,6 +76,21 @@ def test_gemv_argument_validation_on_host(L):
     assert L.moe_expert_gemv_q2k(FAKE, 8, 128, FAKE, 1, FAKE, None) == 2           # K % 256
     assert L.moe_expert_gemv_int4g32(FAKE + 4, FAKE, 8, 64, FAKE, 1, FAKE, None) == 6  # codes misaligned
     assert L.moe_expert_gemv_int4g32(FAKE, None, 8, 64, FAKE, 1, FAKE, None) == 1  # null scales
+
+
+def test_alternative_numerics_validation_on_host(L):
+    assert L.moe_q8k_quantize(None, 1, 256, FAKE, FAKE, None) == 1                  # null x
+    assert L.moe_q8k_quantize(FAKE, 1, 128, FAKE, FAKE, None) == 2                  # K % 256
+    assert L.moe_q8k_quantize(FAKE, 0, 256, FAKE, FAKE, None) == 2                  # B < 1
+    assert L.moe_q8k_quantize(FAKE + 2, 1, 256, FAKE, FAKE, None) == 6              # x misaligned
+    assert L.moe_expert_gemv_mxfp4_q8(FAKE, 8, 256, None, FAKE, 1, FAKE, None) == 1  # null q
+    assert L.moe_expert_gemv_mxfp4_q8(FAKE, 8, 96, FAKE, FAKE, 1, FAKE, None) == 2   # K % 256
+    assert L.moe_expert_gemv_mxfp4_q8(FAKE, 8, 256, FAKE, FAKE, 9, FAKE, None) == 2  # B > 8
+    assert L.moe_expert_gemv_mxfp4_q8(FAKE, 8, 256, FAKE + 8, FAKE, 1, FAKE, None) == 6  # q misaligned
+    assert L.moe_mxfp4_half_lut(None, None) == 1
+    assert L.moe_mxfp4_half_lut(FAKE + 1, None) == 6
+    assert L.moe_expert_gemv_mxfp4_hlut(FAKE, 8, 48, FAKE, 1, FAKE, None) == 2       # K % 32
+    assert L.moe_expert_gemv_mxfp4_hlut(FAKE, 8, 64, FAKE + 4, 1, FAKE, None) == 6   # x misaligned
 
 
 def test_layer_and_route_validation_on_host(L):
