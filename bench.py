@@ -243,7 +243,11 @@ def stack_leg(n_layers: int, seed: int, steps: int, warmup: int, mean_u8: float,
 
 
 def gemv_leg(steps: int, warmup: int, copies: int = 128):
-    """Stand-alone MXFP4 matvec W [2048 x 4096] x fp32 x, rotated over `copies` matrices."""
+    """Stand-alone MXFP4 matvec W [2048 x 4096] x fp32 x, rotated over `copies`
+    matrices: the main path at B=1 (top-level figures), and under "numerics"
+    the main path against the two alternative numerics at B=1 and B=8 -- Q8
+    activations with integer dots (the quantizer launch included, and the
+    matvec alone) and the binary16 table decode."""
     import torch
 
     import quantized_moe_decode_route_amd as moe
@@ -251,23 +255,51 @@ def gemv_leg(steps: int, warmup: int, copies: int = 128):
     stream = torch.cuda.current_stream().cuda_stream
     w = torch.empty(copies * MX_MAT, dtype=torch.uint8, device="cuda")
     synth.gpu_fill("mxfp4", w.data_ptr(), 0x5EED + 9, 0, 0, copies, synth.PROJ_GATE, F * D // 32, stream)
-    x = torch.from_numpy(synth.token_f32(90000, 1, D)).to("cuda")
-    y = torch.empty((1, F), dtype=torch.float32, device="cuda")
-    for i in range(warmup):
-        moe.moe_expert_gemv_mxfp4(w.data_ptr() + (i % copies) * MX_MAT, F, D, x, y)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(steps):
-        moe.moe_expert_gemv_mxfp4(w.data_ptr() + ((warmup + i) % copies) * MX_MAT, F, D, x, y)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+
+    def timed(call):
+        for i in range(warmup):
+            call(w.data_ptr() + (i % copies) * MX_MAT)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(steps):
+            call(w.data_ptr() + ((warmup + i) % copies) * MX_MAT)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    numerics = {}
+    ms_main_b1 = None
+    for B in (1, 8):
+        x = torch.from_numpy(synth.token_f32(90000, B, D)).to("cuda")
+        y = torch.empty((B, F), dtype=torch.float32, device="cuda")
+        q = torch.empty((B, D), dtype=torch.int8, device="cuda")
+        dq = torch.empty((B, D // 256), dtype=torch.float32, device="cuda")
+        moe.moe_q8k_quantize(x, q, dq)
+
+        def q8_full(wp):
+            moe.moe_q8k_quantize(x, q, dq)
+            moe.moe_expert_gemv_mxfp4_q8(wp, F, D, q, dq, y)
+
+        variants = {
+            "main": lambda wp: moe.moe_expert_gemv_mxfp4(wp, F, D, x, y),
+            "q8_with_quantize": q8_full,
+            "q8_matvec_only": lambda wp: moe.moe_expert_gemv_mxfp4_q8(wp, F, D, q, dq, y),
+            "half_table": lambda wp: moe.moe_expert_gemv_mxfp4_hlut(wp, F, D, x, y),
+        }
+        row = {}
+        for name, call in variants.items():
+            ms = timed(call)
+            if B == 1 and name == "main":
+                ms_main_b1 = ms
+            row[name] = {"us_per_call": round(ms * 1e3, 3), "GB/s": round(MX_MAT / (ms * 1e-3) / 1e9, 2)}
+        numerics[f"b{B}"] = row
     del w
     torch.cuda.empty_cache()
-    gbs = MX_MAT / (ms * 1e-3) / 1e9
-    return {"value": round(gbs, 2), "unit": "GB/s", "us_per_call": round(ms * 1e3, 3),
-            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "bytes_per_call": MX_MAT, "copies_rotated": copies}
+    gbs = MX_MAT / (ms_main_b1 * 1e-3) / 1e9
+    return {"value": round(gbs, 2), "unit": "GB/s", "us_per_call": round(ms_main_b1 * 1e3, 3),
+            "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2), "bytes_per_call": MX_MAT, "copies_rotated": copies,
+            "numerics": numerics}
 
 
 def time_layer(layers, xs, B, steps, warmup, ws, idx_log=None):
