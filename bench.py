@@ -346,6 +346,31 @@ def profile_kernel(layers, xs, B, steps, warmup, ws):
 COPY_BYTES = 256 << 20
 
 
+def numerics_pass(n):
+    """Fixed launch order for per-kernel counters of the three matvec numerics:
+    n main MXFP4 matvecs, n Q8 quantizer + integer-dot matvec pairs, n
+    binary16-table matvecs, all on one W [2048 x 4096] and B=8."""
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    import synth
+    stream = torch.cuda.current_stream().cuda_stream
+    w = torch.empty(MX_MAT, dtype=torch.uint8, device="cuda")
+    synth.gpu_fill("mxfp4", w.data_ptr(), 0x5EED + 9, 0, 0, 1, synth.PROJ_GATE, F * D // 32, stream)
+    x = torch.from_numpy(synth.token_f32(90000, 8, D)).to("cuda")
+    y = torch.empty((8, F), dtype=torch.float32, device="cuda")
+    q = torch.empty((8, D), dtype=torch.int8, device="cuda")
+    dq = torch.empty((8, D // 256), dtype=torch.float32, device="cuda")
+    for _ in range(n):
+        moe.moe_expert_gemv_mxfp4(w, F, D, x, y)
+    for _ in range(n):
+        moe.moe_q8k_quantize(x, q, dq)
+        moe.moe_expert_gemv_mxfp4_q8(w, F, D, q, dq, y)
+    for _ in range(n):
+        moe.moe_expert_gemv_mxfp4_hlut(w, F, D, x, y)
+    torch.cuda.synchronize()
+
+
 def counter_pass(layers, x1, x8, ws, n):
     """Fixed launch order for per-dispatch hardware counters: n B=1 layers,
     n B=8 layers, n plain device copies of COPY_BYTES (known traffic)."""
@@ -414,6 +439,9 @@ def main():
                     help="instead of the benchmark: N B=1 layer launches, then N B=8 launches, then N "
                          "copies of a 256 MiB buffer (the copy calibrates HBM byte counters); for "
                          "rocprofv3 --pmc runs")
+    ap.add_argument("--numerics-pass", type=int, default=0, metavar="N",
+                    help="instead of the benchmark: N launches each of the main, Q8 integer-dot and "
+                         "binary16-table MXFP4 matvecs (W 2048 x 4096, B=8), for rocprofv3 --pmc runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this decode path "
@@ -426,6 +454,9 @@ def main():
     import synth
     torch.cuda.set_device(0)
     moe.moe_device_check()
+    if args.numerics_pass:
+        numerics_pass(args.numerics_pass)
+        return
     log(f"building {args.layers} MXFP4 layers ({args.layers * 3 * E * MX_MAT / 1e9:.1f} GB) ...")
     layers = build_layers(args.layers, args.seed, args.down_layout)
     n_tok = args.warmup + args.steps
