@@ -340,7 +340,7 @@ def profile_kernel(layers, xs, B, steps, warmup, ws):
         j = warmup + i
         moe.moe_layer_decode_profiled(layers[j % nl][0], xs[j], y, ws, [e.cuda_event for e in evs[i]])
     torch.cuda.synchronize()
-    return float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)]))
+    return np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)], dtype=np.float64)
 
 
 COPY_BYTES = 256 << 20
@@ -482,8 +482,14 @@ def main():
     gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
 
     log("per-kernel event timing ...")
-    k1 = profile_kernel(layers, x1, 1, args.steps, args.warmup, ws)
-    k8 = profile_kernel(layers, x8, 8, args.steps, args.warmup, ws)
+    k1s = profile_kernel(layers, x1, 1, args.steps, args.warmup, ws)
+    k8s = profile_kernel(layers, x8, 8, args.steps, args.warmup, ws)
+    k1, k8 = float(np.mean(k1s)), float(np.mean(k8s))
+
+    def spread(a):
+        p10, p50, p90 = np.percentile(a * 1e3, [10, 50, 90])
+        return {"mean": round(float(np.mean(a)) * 1e3, 2), "p10": round(p10, 2), "p50": round(p50, 2),
+                "p90": round(p90, 2)}
     # One layer launch per step: the average launch duration is the timed
     # region's HIP-event time on the launch stream divided by the launches.
     # (Events around each launch add their own marker overhead; reported as
@@ -515,6 +521,7 @@ def main():
                "tokens_per_s_layer": round(8e3 / ms8, 1), "mean_unique_experts": round(U8, 2),
                "bytes_per_step": round(bytes8)},
         "launch_bracket_ms": {"b1": round(k1, 5), "b8": round(k8, 5)},
+        "launch_bracket_us_spread": {"b1": spread(k1s), "b8": spread(k8s)},
         "roofline": {"kernel": "fused_layer_kernel (MXFP4, B=1)", "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(), "bytes_per_launch": bytes1, "launch_ms": round(ms1, 5),
