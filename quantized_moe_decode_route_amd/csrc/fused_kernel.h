@@ -265,8 +265,15 @@ struct Rings {  // per format, so a format with more live registers can use shal
   static constexpr int kDN = 7;  // six experts (all of them at B=1) requested ahead
 };
 template <>
-struct Rings<Int4Fmt> {  // its gate/up unpacking keeps more registers live
-  static constexpr int kGU = 4;
+struct Rings<MxFmt> {  // three gate/up items in flight per wave: at the end of gate/up the last items
+                       // are spread over more waves (a 4-slot ring was 0.9 us slower at B=1)
+  static constexpr int kGU = 3;
+  static constexpr int kDN = 7;
+};
+template <>
+struct Rings<Int4Fmt> {  // its gate/up unpacking keeps more registers live; three gate/up slots as for
+                         // MXFP4 (a 4-slot ring was 1.6 us slower at B=1)
+  static constexpr int kGU = 3;
   static constexpr int kDN = 6;
 };
 constexpr int kSpinBatch = 12;  // tagged words a thread reads before its first wait
