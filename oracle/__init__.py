@@ -16,10 +16,13 @@ with plain loops:
   expert); the router keeps the top 6 of 256 experts as "Mixed-precision
   compression of DeepSeek-V4-Flash", "The recipe", requires.
 * ``stack_decode`` -- residual stream carried layer to layer with an
-  unweighted RMSNorm (eps 1e-6) rounded to bfloat16 before each layer.
+  unweighted RMSNorm (eps 1e-6) rounded to bfloat16 before each layer,
+  starting from an fp32 residual state as the stack entry point takes it.
 
-Parity unpinned: the free-running 43-layer composition (each layer and the
-norm are pinned separately).
+Every function is pinned (tests/test_oracle_pins.py); the stack by the
+special cases that fix its composition (zero updates leave the residual
+unchanged, the norm makes layer 0 blind to a power-of-two scale of h_0, and
+equality with the explicit norm -> layer -> residual chain).
 """
 from __future__ import annotations
 
@@ -30,7 +33,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MOE_ORACLE_LIB names another build of oracle.c (the sanitizer test's)
+LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "oracle.c")
 
 FMT_IDS = {"mxfp4": 0, "q2k": 1, "int4g32": 2}
@@ -116,8 +120,28 @@ def lib():
     return _LIB
 
 
+_THREADS = None
+
+
+def host_cores() -> int:
+    """Cores this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
+def set_threads(n: int | None) -> None:
+    """Threads the row-parallel loops use from now on (None: the default)."""
+    global _THREADS
+    _THREADS = None if n is None else max(1, int(n))
+
+
 def default_threads() -> int:
-    return max(1, min(os.cpu_count() or 1, 16))
+    """The host's cores, at most 16 (a one-GPU host's share of its CPU)."""
+    if _THREADS is not None:
+        return _THREADS
+    return max(1, min(host_cores(), 16))
 
 
 def _check(rc: int, what: str) -> None:
@@ -347,16 +371,17 @@ def layer_decode(fmt, get_expert, wr: np.ndarray, x_bf16: np.ndarray, top_k: int
     return y, idx, g
 
 
-def stack_decode(fmt, get_layer_expert, routers, x_bf16: np.ndarray, top_k: int = 6,
+def stack_decode(fmt, get_layer_expert, routers, h0: np.ndarray, top_k: int = 6,
                  d_ff: int | None = None, eps: float = 1e-6, trace: bool = False):
-    """Residual stream through ``len(routers)`` layers: x_l = bf16(rmsnorm(h_l)),
-    h_{l+1} = h_l + moe_l(x_l), h_0 = x (the activation's exact value).
+    """Residual stream through ``len(routers)`` layers, from the residual state
+    ``h0`` ([B, D], fp32 or fp64 values, taken exactly): x_l = bf16(rmsnorm(h_l)),
+    h_{l+1} = h_l + moe_l(x_l), in fp64.
 
     ``get_layer_expert(l, e)`` returns layer l's expert e weights.  Returns the
-    final h (fp64 [B, D]) and, if ``trace``, the per-layer (x_l, idx_l, g_l).
+    final h (fp64 [B, D]) and, if ``trace``, the per-layer (x_l, idx_l, g_l, y_l).
     """
     D = routers[0].shape[1]
-    h = bf16_rows_to_f64(np.asarray(x_bf16, dtype=np.uint16).reshape(-1, D))
+    h = np.array(h0, dtype=np.float64).reshape(-1, D)
     steps = []
     for l, wr in enumerate(routers):
         xl = rmsnorm_bf16(h, eps)

@@ -30,8 +30,8 @@
  *           exactly rounded binary16 products) and "MXFP4's ROCm native
  *           kernel" (activations quantized to Q8_K, integer dot products).
  *
- * Parity unpinned: none of the functions below lacks a pin, except that the
- * composition of 43 stacked layers is checked only layer by layer.
+ * Every function below is pinned by tests/test_oracle_pins.py (the stacked
+ * composition, in oracle/__init__.py, by its special cases as well).
  */
 #include <math.h>
 #include <pthread.h>

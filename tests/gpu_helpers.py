@@ -6,6 +6,8 @@ Expected values always come from ``oracle`` on inputs produced by ``synth``
 (never from the HIP path)."""
 from __future__ import annotations
 
+import copy
+
 import numpy as np
 import torch
 
@@ -65,8 +67,12 @@ class Layer:
     """
 
     def __init__(self, fmt: str, seed: int, layer: int, E: int, D: int, F: int, top_k: int = 6,
-                 down_layout: str = "rows", down_fmt: str | None = None):
+                 down_layout: str = "rows", down_fmt: str | None = None, mutate=None):
         self.fmt, self.seed, self.layer = fmt, seed, layer
+        # mutate(proj, expert, bytes) -> bytes: an edit of the seeded MXFP4 or
+        # Q2_K bytes applied on both sides (the device copy is then uploaded
+        # from the host instead of filled on the GPU; small shapes only)
+        self.mutate = mutate
         self.down_fmt = down_fmt or fmt
         self.E, self.D, self.F, self.k = E, D, F, top_k
         self.down_layout = down_layout
@@ -85,7 +91,12 @@ class Layer:
             buf = torch.empty(E * stride, dtype=torch.uint8, device="cuda")
             bw, bb = BLOCK[src]
             for e in range(E):
-                synth.gpu_fill(src, buf.data_ptr() + e * stride, seed, layer, e, 1, proj, n * (kk // bw), stream)
+                if mutate is None:
+                    synth.gpu_fill(src, buf.data_ptr() + e * stride, seed, layer, e, 1, proj, n * (kk // bw),
+                                   stream)
+                else:
+                    hb = mutate(proj, e, synth.expert_tensor(src, seed, layer, e, proj, n, kk).copy())
+                    buf[e * stride:e * stride + hb.size].copy_(torch.from_numpy(hb))
             tiled = proj == synth.PROJ_DOWN and down_layout != "rows"
             if pf == "int4g32":
                 qstride = n * kk // 2
@@ -131,11 +142,25 @@ class Layer:
             pf = self.pfmt[proj]
             n, kk = self.shape[proj]
             b = synth.expert_tensor("mxfp4" if pf == "int4g32" else pf, self.seed, self.layer, e, proj, n, kk)
+            if self.mutate is not None:
+                b = self.mutate(proj, e, b.copy())
             if pf == "int4g32":
                 b = oracle.quantize_fp4_to_int4g32(b, n, kk)
             mats.append(b)
         self._cache[e] = tuple(mats)
         return self._cache[e]
+
+    def with_router(self, wr: np.ndarray) -> "Layer":
+        """The same experts under another router matrix (fp32 [E, D]): a new
+        descriptor pointing at a device copy of ``wr``, which the oracle side
+        uses too.  The expert tensors and the oracle's expert cache are shared."""
+        other = copy.copy(self)
+        other.router = np.ascontiguousarray(wr, dtype=np.float32)
+        assert other.router.shape == (self.E, self.D)
+        other.router_dev = dev(other.router)
+        other.desc = type(self.desc).from_buffer_copy(self.desc)
+        other.desc.router_w = other.router_dev.data_ptr()
+        return other
 
     def workspace(self, B: int) -> torch.Tensor:
         nbytes = moe.moe_layer_workspace_bytes(B, self.D, self.F, self.E, self.k)

@@ -116,3 +116,29 @@ def test_gemv_rejects_bad_arguments():
     x9 = torch.zeros((9, 64), dtype=torch.float32, device="cuda")
     with pytest.raises(moe.MoeError):
         moe.moe_expert_gemv_mxfp4(w, 8, 64, x9, y)     # B > 8
+
+
+def _with_exponents(blocks, choices, seed):
+    b = blocks.reshape(-1, 17).copy()
+    b[:, 0] = np.random.default_rng(seed).choice(np.asarray(choices, dtype=np.uint8), size=b.shape[0])
+    return b.reshape(-1)
+
+
+@pytest.mark.parametrize("case", ["low", "high", "mixed"])
+@pytest.mark.parametrize("B", [1, 8])
+def test_gemv_mxfp4_e8m0_extremes(case, B):
+    """Scale bytes at both ends of the E8M0 range: 0 (2^-127, whose fp32 bit
+    pattern is subnormal), 1, 2, and 250..254 (up to 2^127), alone or mixed
+    with the ordinary 118..134.  x is scaled by a power of two so that every
+    result is a finite fp32 number (for the mixed rows the tiny blocks then
+    contribute below fp32 resolution)."""
+    n, k = 64, 1024
+    choices, shift = {"low": ([0, 1, 2], 40), "high": ([250, 251, 252, 253, 254], -40),
+                      "mixed": ([0, 1, 2, 120, 127, 134, 250, 254], -110)}[case]
+    w = _with_exponents(_mx(61, n, k), choices, 62)
+    x = np.ldexp(synth.token_f32(63 + B, B, k).astype(np.float64), shift).astype(np.float32)
+    y = _run("mxfp4", w, n, k, x)
+    ref = oracle.gemv("mxfp4", w, n, k, x.astype(np.float64))
+    assert np.all(np.isfinite(ref)) and np.all(np.abs(ref) < 1e37)
+    assert np.all(np.isfinite(y))
+    assert_parity(y, ref, what=f"E8M0 {case} B={B}")

@@ -148,3 +148,30 @@ def test_traced_records_stay_in_bounds():
     assert ((t[:nb.value, 6] <= t[:nb.value, 11]) & (t[:nb.value, 11] <= t[:nb.value, 12])
             & (t[:nb.value, 12] <= t[:nb.value, 7])).all()
     assert (t[:nb.value, 14] < 16).all()
+
+
+def _extreme_exponents(proj, e, b):
+    """A quarter of the blocks of every MXFP4 projection get scale bytes 0, 1
+    or 2 (2^-127 .. 2^-125); for the down projection another eighth get
+    160..170, large but with every result finite in fp32."""
+    blk = b.reshape(-1, 17)
+    rng = np.random.default_rng(1000 * proj + e)
+    pick = rng.random(blk.shape[0])
+    blk[pick < 0.25, 0] = rng.integers(0, 3, size=int((pick < 0.25).sum()))
+    if proj == synth.PROJ_DOWN:
+        big = (pick >= 0.25) & (pick < 0.375)
+        blk[big, 0] = rng.integers(160, 171, size=int(big.sum()))
+    return blk.reshape(-1)
+
+
+@pytest.mark.parametrize("layout", MX_LAYOUTS)
+@pytest.mark.parametrize("B", [1, 8])
+def test_layer_e8m0_extremes(layout, B):
+    """Tiny and large E8M0 scale bytes through the single-launch layer (the
+    gate/up conversion multiplies by the subnormal 2^-127 for byte 0, the
+    matrix-core down path passes the byte as the MFMA A scale)."""
+    L = Layer("mxfp4", 0x5EED + 70, 0, 16, 512, 256, 6, down_layout=layout, mutate=_extreme_exponents)
+    assert _single_launch(L, B)
+    xb = synth.token_bf16(8000 + B, B, 512)
+    err, y = _parity(L, xb, f"E8M0 extremes B={B} {layout}")
+    assert np.all(np.isfinite(y))

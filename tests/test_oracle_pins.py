@@ -455,6 +455,60 @@ def test_rmsnorm_closed_forms():
     assert np.allclose(out, h / rms, rtol=2 ** -8)
 
 
+
+# ------------------------------------------------------------------ stack
+
+def _tiny_stack(n_layers, seed, zero_down=False):
+    rng = np.random.default_rng(seed)
+    E, D, F = 8, 64, 32
+    experts = []
+    for _ in range(n_layers):
+        lay = []
+        for _ in range(E):
+            g, u, d = _rand_mx(F, D, rng), _rand_mx(F, D, rng), _rand_mx(D, F, rng)
+            if zero_down:
+                d = d.reshape(-1, 17).copy()
+                d[:, 1:] = 0          # every code 0: the down projection is the zero matrix
+                d = d.reshape(-1)
+            lay.append((g, u, d))
+        experts.append(lay)
+    routers = [(rng.standard_normal((E, D)) * 0.05).astype(np.float32) for _ in range(n_layers)]
+    h0 = (rng.standard_normal((3, D)) * 2.0).astype(np.float32)
+    return experts, routers, h0, F
+
+
+def test_stack_zero_updates_keep_the_residual():
+    experts, routers, h0, F = _tiny_stack(3, 31, zero_down=True)
+    h = oracle.stack_decode("mxfp4", lambda l, e: experts[l][e], routers, h0, 2, F)
+    assert np.array_equal(h, h0.astype(np.float64))
+
+
+def test_stack_norm_hides_a_power_of_two_scale():
+    # With eps = 0 the norm of 4 h equals the norm of h exactly, so layer 0
+    # sees the same activation and adds the same update to the scaled state.
+    experts, routers, h0, F = _tiny_stack(1, 32)
+    get = lambda l, e: experts[l][e]
+    h_a, (step_a,) = oracle.stack_decode("mxfp4", get, routers, h0, 2, F, eps=0.0, trace=True)
+    h4 = (h0 * np.float32(4.0)).astype(np.float32)
+    h_b, (step_b,) = oracle.stack_decode("mxfp4", get, routers, h4, 2, F, eps=0.0, trace=True)
+    assert np.array_equal(step_a[0], step_b[0]) and np.any(step_a[0] != 0)
+    assert np.array_equal(step_a[3], step_b[3])
+    assert np.array_equal(h_b, h4.astype(np.float64) + step_a[3])
+    assert not np.array_equal(h_a, h_b)
+
+
+def test_stack_equals_explicit_norm_layer_residual_chain():
+    experts, routers, h0, F = _tiny_stack(2, 33)
+    h, steps = oracle.stack_decode("mxfp4", lambda l, e: experts[l][e], routers, h0, 2, F, trace=True)
+    cur = h0.astype(np.float64)
+    for l in range(2):
+        x = oracle.rmsnorm_bf16(cur, 1e-6)
+        y, idx, g = oracle.layer_decode("mxfp4", lambda e, _l=l: experts[_l][e], routers[l], x, 2, F)
+        assert np.array_equal(x, steps[l][0]) and np.array_equal(idx, steps[l][1])
+        cur = cur + y
+    assert np.array_equal(h, cur)
+
+
 # ------------------------------------------------------------------ FP4 -> INT4
 
 def test_int4_candidates_from_pages():
