@@ -49,11 +49,12 @@ FusedShape fused_shape(int fmt, int dfmt, int B, int k, int D, int F, int grid, 
   size_t down = (size_t)B * k * ups * (uw + 4) * 4 + (size_t)B * k * rpwd * 4;
   if (sh.mfma) {
     // one 16-row tile per wave, at most two 128-column k-steps per XCD
-    // slice; the B operands and row partials sit beside the activations
+    // slice; the B operands (kHTerms E4M3 terms of 128 values per k-step and
+    // slot, plus the zero slot) and row partials replace the activations
     if (rpv > 16 || ups > 8) return sh;
     const size_t S = (size_t)B * k, dnk = (ups + 3) / 4;
     auto up16 = [](size_t v) { return (v + 15) & ~(size_t)15; };
-    down = up16(act) + (S + 1) * dnk * 512 + up16((S + 1) * 4 * dnk) + S * rpwd * 4;
+    down = (S + 1) * dnk * 128 * fused::kHTerms + up16((S + 1) * 4 * dnk) + S * rpwd * 4;
   }
   if (act > (size_t)kLdsBytes || down > (size_t)kLdsBytes) return sh;
   sh.ok = true;

@@ -277,6 +277,13 @@ struct Rings<Int4Fmt> {  // its gate/up unpacking keeps more registers live; thr
   static constexpr int kDN = 6;
 };
 constexpr int kSpinBatch = 12;  // tagged words a thread reads before its first wait
+// Matrix-core down projection: h enters the MFMA as kHTerms E4M3 terms per
+// value, term i scaled by 2^(-kHTermStep * i) relative to term 0, and one
+// token takes kHCols of the 16 B columns (its terms, then zero columns).
+constexpr int kHTerms = 6;
+constexpr int kHTermStep = 4;
+constexpr int kHCols = 8;
+static_assert(kHTerms <= kHCols && 16 % kHCols == 0, "a token's terms fit its columns");
 constexpr int kPrefetchExperts = 1;  // one token: experts whose gate/up rows go to L2 during top-k
 constexpr bool kPrefetchDown = true;  // ... and their down rows
 
@@ -715,12 +722,6 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       }
     }
   }
-  if constexpr (DNK > 0) {  // the zero B operand (slot S) read by lanes without a token
-    uint8_t* hb0 = s_buf + (((size_t)B * UG * kCh * 16 + 15) & ~(size_t)15);
-    for (int i = threadIdx.x; i < DNK * 512 / 16; i += kW * kWave)
-      reinterpret_cast<uint4*>(hb0 + (size_t)S * DNK * 512)[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (threadIdx.x < 4 * DNK) hb0[(size_t)(S + 1) * DNK * 512 + S * 4 * DNK + threadIdx.x] = 0;
-  }
   __syncthreads();
   stamp(a, 4);
   // Group (token, rank) pairs by expert, experts ascending: one record per
@@ -795,13 +796,15 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   const int RPV = (RPWd + kW - 1) / kW;          // rows per wave
   const int n0 = jx * RPWd;
   // Matrix-core down projection (MXFP4 in MOE_LAYOUT_MFMA16, DNK > 0): the
-  // h slice goes to LDS as fp32 [S][FS], then as the B operand of the
-  // 16x16x128 scaled MFMA: four fp8 (E4M3) terms per value, h = 2^(e-127) *
-  // (c0 + c1 + c2 + c3), one E8M0 e per 32 values.  hb: [S][DNK][4 lane
-  // groups][4 terms][32 bytes]; hsc: [S][4 * DNK] exponents.
-  // Slot S of hb/hsc is all zeros: lanes without a token read it.
-  constexpr int kHbSlot = DNK * 512;
-  uint8_t* hb = s_buf + (((size_t)B * UG * kCh * 16 + 15) & ~(size_t)15);  // after the activations
+  // h slice of every slot becomes the B operand of the 16x16x128 scaled
+  // MFMA as kHTerms fp8 (E4M3) terms per value, each term with its own E8M0
+  // exponent: h = sum_i c_i * 2^(e - 4i - 127), c_i a multiple of 16 in
+  // [-256, 256], one e per 32 values (see gather_batch).  hb: [S][DNK][4 lane groups][kHTerms terms][32 bytes];
+  // hsc: [S][4 * DNK] exponents e.  Both take the LDS of the activations,
+  // which are dead once gate/up has ended.  Slot S of hb/hsc is all zeros:
+  // lanes without a token (or term) read it.
+  constexpr int kHbSlot = DNK * 4 * kHTerms * 32;
+  uint8_t* hb = s_buf;
   uint8_t* hsc = hb + (size_t)(S + 1) * kHbSlot;
   float* syp = DNK > 0 ? reinterpret_cast<float*>(hsc + (((size_t)(S + 1) * 4 * DNK + 15) & ~(size_t)15))
                        : sh + (size_t)S * UPS * kHB;  // [S][rows of this workgroup]
@@ -901,8 +904,16 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = valid[4 * b + i] ? __uint_as_float(payload_of(v[4 * b + i])) : 0.0f;
       // The 8 lanes of a 32-value block agree on its exponent e, which puts
-      // the block maximum in [128, 256): every term stays a normal or zero
-      // E4M3 value well inside its range.
+      // the block maximum in [128, 256) once scaled by 2^(127 - e).  The
+      // terms are base-16 digits of that scaled value: term i is the multiple
+      // of 16 nearest to what the earlier terms left, scaled by 2^(4i) (E8M0
+      // exponent e_i = e - 4i), so every term lies in {0, +-16, ..., +-256},
+      // is exact in E4M3, and the B values of one column span only the
+      // binades 2^4 .. 2^8.  (The scaled MFMA sums products whose exponents
+      // lie in such a narrow band exactly; a B column holding values from all
+      // of E4M3's range loses the smallest products.)  A remainder is at most
+      // 8, 128 once scaled by 2^4; six terms leave |error| <= 2^-24 * the
+      // block maximum (fp32 resolution).
       float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
       mx = fmaxf(mx, dpp_f<0xB1>(mx));   // quad_perm [1,0,3,2]
       mx = fmaxf(mx, dpp_f<0x4E>(mx));   // quad_perm [2,3,0,1]
@@ -911,24 +922,27 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       const float scale = __uint_as_float((uint32_t)(254 - e) << 23);  // 2^(127 - e), exact
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] *= scale;
-      // hb byte q of lane group g, k-step ks holds value 128ks + 64(q/16) +
-      // 16g + ((q%16)^1): the E2M1 nibble order pairs weight 2j+1 with the
-      // lower K position, so values are stored pair-swapped.
+      // hb byte q of lane group g, k-step ks, term i holds value 128ks +
+      // 64(q/16) + 16g + ((q%16)^1): the E2M1 nibble order pairs weight 2j+1
+      // with the lower K position, so values are stored pair-swapped.
       const int r = fl & 127, ks = fl >> 7;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(hb + (size_t)sl[b] * kHbSlot +
-                                                  ((ks * 4 + ((r & 63) >> 4)) * 4) * 32 + (r >> 6) * 16 + (r & 15));
+      uint32_t* dst = reinterpret_cast<uint32_t*>(
+          hb + (size_t)sl[b] * kHbSlot + ((ks * 4 + ((r & 63) >> 4)) * kHTerms) * 32 + (r >> 6) * 16 + (r & 15));
+      int et = e;
 #pragma unroll
-      for (int term = 0; term < 4; ++term) {
-        int d = __builtin_amdgcn_cvt_pk_fp8_f32(x[1], x[0], 0, false);
-        d = __builtin_amdgcn_cvt_pk_fp8_f32(x[3], x[2], d, true);
+      for (int term = 0; term < kHTerms; ++term) {
+        float t[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] = 16.0f * __builtin_rintf(x[i] * 0.0625f);  // exact multiple of 16
+        int d = __builtin_amdgcn_cvt_pk_fp8_f32(t[1], t[0], 0, false);
+        d = __builtin_amdgcn_cvt_pk_fp8_f32(t[3], t[2], d, true);
         if (act) dst[term * 8] = (uint32_t)d;
-        if (term < 3) {
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(d, false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(d, true);
-          x[1] -= lo.x;
-          x[0] -= lo.y;
-          x[3] -= hi.x;
-          x[2] -= hi.y;
+        if (term + 1 < kHTerms) {
+          const int en = max(et - kHTermStep, 0);
+          const float up = __uint_as_float((uint32_t)(127 + et - en) << 23);  // 2^(e_i - e_(i+1)), exact
+          et = en;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = (x[i] - t[i]) * up;  // exact
         }
       }
       if (act && (lane & 7) == 0) hsc[sl[b] * 4 * DNK + (fl >> 5)] = (uint8_t)e;
@@ -956,26 +970,29 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       const int T = __builtin_popcount(mask & 0xFFu);
       const uint32_t slo = (uint32_t)__builtin_amdgcn_readlane((int)gsl_lo, uu);
       const uint32_t shi = (uint32_t)__builtin_amdgcn_readlane((int)gsl_hi, uu);
-      const int c = mi & 3;
-      for (int p0 = 0; p0 < T; p0 += 4) {  // four tokens (x four terms) per pass
-        const int tt = p0 + (mi >> 2);
+      const int c = mi % kHCols;  // the column's term (none past kHTerms)
+      for (int p0 = 0; p0 < T; p0 += 16 / kHCols) {  // two tokens (x eight columns) per pass
+        const int tt = p0 + mi / kHCols;
         const bool tok = tt < T;
-        const int sl = tok ? (int)(((tt < 4 ? slo : shi) >> (8 * (tt & 3))) & 0xFFu) : S;
+        const int sl = tok && c < kHTerms ? (int)(((tt < 4 ? slo : shi) >> (8 * (tt & 3))) & 0xFFu) : S;
+        const int ct = c < kHTerms ? c : 0;
         v4f acc[DNK];
 #pragma unroll
         for (int ks = 0; ks < DNK; ++ks) {
-          const uint4* bp = reinterpret_cast<const uint4*>(hb + (size_t)sl * kHbSlot + ((ks * 4 + mg) * 4 + c) * 32);
+          const uint4* bp =
+              reinterpret_cast<const uint4*>(hb + (size_t)sl * kHbSlot + ((ks * 4 + mg) * kHTerms + ct) * 32);
           const uint4 b0 = bp[0], b1 = bp[1];
-          const int eb = hsc[sl * 4 * DNK + 4 * ks + mg];
+          const int eb = max((int)hsc[sl * 4 * DNK + 4 * ks + mg] - kHTermStep * ct, 0);
           const v8i Bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
           acc[ks] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[ks], Bv, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 0, 0,
                                                                      ea[ks], 0, eb);
         }
 #pragma unroll
         for (int ks = 1; ks < DNK; ++ks) acc[0] += acc[ks];  // k-steps in order
-        // lane (tt, term c) holds rows 4mg..4mg+3 of column 4tt+c: sum the terms
+        // lane (tt, column c) holds rows 4mg..4mg+3 of column kHCols*tt + c:
+        // sum the token's terms
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[0][r] = group_sum_dpp<4>(acc[0][r]);
+        for (int r = 0; r < 4; ++r) acc[0][r] = group_sum_dpp<kHCols>(acc[0][r]);
         if (tok && c == 0) {
           if (dn_full) {  // the wave's 16 rows are all in range: one 16-byte store
             *reinterpret_cast<float4*>(syp + sl * RPWd + w * 16 + 4 * mg) =
@@ -1028,7 +1045,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       constexpr int j0 = decltype(j0c)::value;
       typedef int v8i __attribute__((ext_vector_type(8)));
       typedef float v4f __attribute__((ext_vector_type(4)));
-      const int c = mi & 3, tt = mi >> 2;
+      const int c = mi % kHCols, tt = mi / kHCols;
+      const int ct = c < kHTerms ? c : 0;
       v8i A[kDnBatch][DNK], Bv[kDnBatch][DNK];
       int ea[kDnBatch][DNK], eb[kDnBatch][DNK], sl[kDnBatch];
       bool st[kDnBatch];
@@ -1042,7 +1060,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         const int T = live ? __builtin_popcount(mask & 0xFFu) : 0;
         const bool tok = tt < T;
         const uint32_t tab = (uint32_t)__builtin_amdgcn_readlane((int)gsl_lo, live ? j : U - 1);
-        sl[b] = tok ? (int)((tab >> (8 * (tt & 3))) & 0xFFu) : S;
+        sl[b] = tok && c < kHTerms ? (int)((tab >> (8 * (tt & 3))) & 0xFFu) : S;
         st[b] = tok && c == 0;
 #pragma unroll
         for (int ks = 0; ks < DNK; ++ks) {
@@ -1050,10 +1068,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
           FD::unpack(dring[j][ks], (uint32_t)dblk[ks] & 3u, e, q);
           A[b][ks] = v8i{(int)q[0], (int)q[1], (int)q[2], (int)q[3], 0, 0, 0, 0};
           ea[b][ks] = (int)e;
-          const uint4* bp = reinterpret_cast<const uint4*>(hb + (size_t)sl[b] * kHbSlot + ((ks * 4 + mg) * 4 + c) * 32);
+          const uint4* bp =
+              reinterpret_cast<const uint4*>(hb + (size_t)sl[b] * kHbSlot + ((ks * 4 + mg) * kHTerms + ct) * 32);
           const uint4 b0 = bp[0], b1 = bp[1];
           Bv[b][ks] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-          eb[b][ks] = hsc[sl[b] * 4 * DNK + 4 * ks + mg];
+          eb[b][ks] = max((int)hsc[sl[b] * 4 * DNK + 4 * ks + mg] - kHTermStep * ct, 0);
         }
       }
 #pragma unroll
@@ -1068,7 +1087,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
         for (int ks = 1; ks < DNK; ++ks) acc[0] += acc[ks];  // k-steps in order
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[0][r] = group_sum_dpp<4>(acc[0][r]);
+        for (int r = 0; r < 4; ++r) acc[0][r] = group_sum_dpp<kHCols>(acc[0][r]);
         if (st[b])
           *reinterpret_cast<float4*>(syp + sl[b] * RPWd + w * 16 + 4 * mg) =
               make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
@@ -1236,8 +1255,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
   }
   if constexpr (DNK > 0) {
-    __syncthreads();  // every row of this workgroup is published
+    __syncthreads();  // every row of this workgroup is published; the activations are dead
     stamp(a, 11);
+    // the zero B operand and exponents (slot S), read by lanes without a token or term
+    for (int i = threadIdx.x; i < kHbSlot / 16; i += kW * kWave)
+      reinterpret_cast<uint4*>(hb + (size_t)S * kHbSlot)[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (threadIdx.x < 4 * DNK) hsc[S * 4 * DNK + threadIdx.x] = 0;
     if (S <= kW) {
       while (gather_batch(std::integral_constant<int, 1>{})) {
       }
@@ -1250,9 +1273,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     __syncthreads();
   }
   stamp(a, 7);
-  if (DNK > 0 && dn_walk && B <= 4 && dn_full) {
+  if (DNK > 0 && dn_walk && B <= 16 / kHCols && dn_full) {
     // Every group's down weights are in the prologue slots and every group
-    // has at most 4 tokens (one MFMA pass): the groups are computed in
+    // has at most two tokens (one MFMA pass): the groups are computed in
     // straight-line batches, so their LDS reads and MFMAs overlap.
     down_walk_batch(std::integral_constant<int, 0>{});
     down_walk_batch(std::integral_constant<int, kDnBatch>{});
