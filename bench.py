@@ -192,15 +192,17 @@ def format_leg(fmt: str, n_layers: int, seed: int, steps: int, warmup: int, ws):
     for B in (1, 8):
         xs = [torch.from_numpy(synth.token_bf16(50000 + 97 * B + i, B, D).view(np.int16)).to("cuda")
               for i in range(warmup + steps)]
+        xs_settle = [torch.from_numpy(synth.token_bf16(55000 + 97 * B + i, B, D).view(np.int16)).to("cuda")
+                     for i in range(16)]
         idx_log = torch.empty((steps, B, TOPK), dtype=torch.int32, device="cuda")
-        ms, _ = time_layer(layers, xs, B, steps, warmup, ws, idx_log)
+        ms, _, st = time_layer(layers, xs, B, steps, warmup, ws, idx_log, xs_settle)
         U = float(np.mean([len(np.unique(r)) for r in idx_log.cpu().numpy()]))
         nbytes = U * EXPERT_BYTES[fmt] + ROUTER
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[f"b{B}"] = {"value": round(gbs, 2), "unit": "GB/s", "ms_per_step": round(ms, 5),
                         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
                         "tokens_per_s_layer": round(B * 1e3 / ms, 1), "mean_unique_experts": round(U, 2),
-                        "bytes_per_step": round(nbytes)}
+                        "bytes_per_step": round(nbytes), "settle": st}
     del layers
     torch.cuda.empty_cache()
     return out
@@ -220,22 +222,26 @@ def stack_leg(n_layers: int, seed: int, steps: int, warmup: int, mean_u8: float,
     out = {"layers": n_layers, "format": fmt, "resident_bytes": n_layers * (E * EXPERT_BYTES[fmt] + ROUTER)}
     for B in (1, 8):
         hs = [torch.from_numpy(synth.token_f32(70000 + 31 * B + i, B, D)).to("cuda") for i in range(warmup + steps)]
+        hs_settle = [torch.from_numpy(synth.token_f32(75000 + 31 * B + i, B, D)).to("cuda") for i in range(4)]
         hout = torch.empty((B, D), dtype=torch.float32, device="cuda")
+        s = torch.cuda.current_stream().cuda_stream
+        st = settle(lambda i: moe.moe_stack_decode(descs, hs_settle[i], hout, ws, stream=s), len(hs_settle))
         for i in range(warmup):
-            moe.moe_stack_decode(descs, hs[i], hout, ws)
+            moe.moe_stack_decode(descs, hs[i], hout, ws, stream=s)
         torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
         for i in range(steps):
-            moe.moe_stack_decode(descs, hs[warmup + i], hout, ws)
+            moe.moe_stack_decode(descs, hs[warmup + i], hout, ws, stream=s)
         end.record()
         torch.cuda.synchronize()
+        check_flags(ws, f"stack B={B}")
         ms = start.elapsed_time(end) / steps
         u = TOPK if B == 1 else mean_u8
         nbytes = n_layers * (u * EXPERT_BYTES[fmt] + ROUTER)
         out[f"b{B}"] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(B * 1e3 / ms, 1),
                         "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
-                        "bytes_per_step": round(nbytes),
+                        "bytes_per_step": round(nbytes), "settle": st,
                         "bytes_note": "exact" if B == 1 else "mean unique experts per layer taken from the B=8 layer leg"}
     del layers, descs
     torch.cuda.empty_cache()
@@ -302,45 +308,91 @@ def gemv_leg(steps: int, warmup: int, copies: int = 128):
             "numerics": numerics}
 
 
-def time_layer(layers, xs, B, steps, warmup, ws, idx_log=None):
+SETTLE_MS = 40.0          # untimed GPU work before every timed leg, whatever --warmup says
+SETTLE_MIN_LAUNCHES = 64
+
+
+def check_flags(ws, what: str) -> None:
+    """Exit non-zero if a bounded wait in a layer kernel gave up (its results
+    would be wrong) or a hash-routed layer met an invalid id."""
+    import quantized_moe_decode_route_amd as moe
+    f = moe.moe_workspace_flags(ws)
+    if f:
+        log(f"{what}: workspace flags {f:#x} (bit 0: a wait timed out; bit 1: invalid hash-routing input)")
+        sys.exit(3)
+
+
+def settle(launch, n_inputs: int) -> dict:
+    """Runs launch(i) (i cycles over n_inputs inputs that the timed region does
+    not use) until SETTLE_MS of GPU time and SETTLE_MIN_LAUNCHES launches have
+    passed, so clocks and caches are in their steady state when timing starts."""
+    import torch
+    n, ms = 0, 0.0
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    while ms < SETTLE_MS or n < SETTLE_MIN_LAUNCHES:
+        start.record()
+        for _ in range(16):
+            launch(n % n_inputs)
+            n += 1
+        end.record()
+        end.synchronize()
+        ms += start.elapsed_time(end)
+    return {"launches": n, "ms": round(ms, 2)}
+
+
+def time_layer(layers, xs, B, steps, warmup, ws, idx_log=None, xs_settle=None):
+    """Average ms per step over `steps` layer launches (fresh token each, layer
+    instances rotated), after a settle pass on other tokens and `warmup`
+    untimed steps.  Returns (ms, host wall ms per step, settle record)."""
     import torch
 
     import quantized_moe_decode_route_amd as moe
     y = torch.empty((B, D), dtype=torch.float32, device="cuda")
     nl = len(layers)
+    s = torch.cuda.current_stream().cuda_stream
+    st = None
+    if xs_settle:
+        st = settle(lambda i: moe.moe_layer_decode(layers[(i + 3) % nl][0], xs_settle[i], y, ws, stream=s),
+                    len(xs_settle))
     for i in range(warmup):
-        moe.moe_layer_decode(layers[i % nl][0], xs[i], y, ws)
+        moe.moe_layer_decode(layers[i % nl][0], xs[i], y, ws, stream=s)
+    idx_rows = [idx_log[i] for i in range(steps)] if idx_log is not None else [None] * steps
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     start.record()
     for i in range(steps):
         j = warmup + i
-        moe.moe_layer_decode(layers[j % nl][0], xs[j], y, ws, idx_log[i] if idx_log is not None else None)
+        moe.moe_layer_decode(layers[j % nl][0], xs[j], y, ws, idx_rows[i], stream=s)
     end.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    return start.elapsed_time(end) / steps, t_wall / steps * 1e3
+    check_flags(ws, f"layer B={B}")
+    return start.elapsed_time(end) / steps, t_wall / steps * 1e3, st
 
 
-def profile_kernel(layers, xs, B, steps, warmup, ws):
-    """Average duration of the layer's kernel launch, from hipEvents recorded
-    on the launch stream right before and after it."""
+def profile_kernel(layers, xs, B, ws):
+    """Duration of each layer launch, from hipEvents recorded on the launch
+    stream right before and after it (tokens of their own, not the timed
+    region's)."""
     import torch
 
     import quantized_moe_decode_route_amd as moe
     y = torch.empty((B, D), dtype=torch.float32, device="cuda")
     nl = len(layers)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    s = torch.cuda.current_stream().cuda_stream
+    n = len(xs)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
     for row in evs:
         for e in row:
             e.record()
     torch.cuda.synchronize()
-    for i in range(steps):
-        j = warmup + i
-        moe.moe_layer_decode_profiled(layers[j % nl][0], xs[j], y, ws, [e.cuda_event for e in evs[i]])
+    for i in range(n):
+        moe.moe_layer_decode_profiled(layers[(i + 5) % nl][0], xs[i], y, ws, [e.cuda_event for e in evs[i]],
+                                      stream=s)
     torch.cuda.synchronize()
-    return np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(steps)], dtype=np.float64)
+    check_flags(ws, f"bracketed layer B={B}")
+    return np.array([evs[i][0].elapsed_time(evs[i][1]) for i in range(n)], dtype=np.float64)
 
 
 COPY_BYTES = 256 << 20
@@ -392,7 +444,9 @@ def counter_pass(layers, x1, x8, ws, n):
 
 
 def cpu_baseline(seed: int, n_tokens: int):
-    """The oracle on the host cores: B=1 layer decode for a few tokens."""
+    """The oracle on the host: B=1 layer decode of a few tokens, timed on one
+    thread and on every core this process may use (threads split output rows;
+    at most 16, a one-GPU host's share of its CPU)."""
     import oracle
     import synth
     wr = synth.router_weights(seed, 0, E, D)
@@ -409,16 +463,29 @@ def cpu_baseline(seed: int, n_tokens: int):
         idx, _, _ = oracle.route_topk(wr, x, TOPK)
         for e in idx[0]:
             get(int(e))
-    t = time.perf_counter()
-    for x in xs:
-        oracle.layer_decode("mxfp4", get, wr, x, TOPK, F)
-    dt = (time.perf_counter() - t) / n_tokens
     bytes_step = TOPK * 3 * MX_MAT + ROUTER
-    return {"value": round(bytes_step / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.default_threads(),
+    cores = oracle.host_cores()
+
+    def timed(threads, toks):
+        oracle.set_threads(threads)
+        try:
+            t = time.perf_counter()
+            for x in toks:
+                oracle.layer_decode("mxfp4", get, wr, x, TOPK, F)
+            return (time.perf_counter() - t) / len(toks)
+        finally:
+            oracle.set_threads(None)
+
+    threads = oracle.default_threads()
+    dt_all = timed(threads, xs)
+    dt_one = timed(1, xs[:max(1, n_tokens // 3)])
+    return {"value": round(bytes_step / dt_all / 1e9, 4), "unit": "GB/s", "cores": cores, "threads": threads,
             "kind": "oracle",
-            "sample": f"{n_tokens} B=1 tokens through one 256-expert MXFP4 layer (fp64 oracle, "
-                      f"{dt:.2f} s per token; expert bytes drawn before timing)",
-            "seconds_per_token_layer": round(dt, 4)}
+            "sample": f"{n_tokens} B=1 tokens through one 256-expert MXFP4 layer (fp64 oracle on {threads} "
+                      f"threads of {cores} cores, {dt_all:.3f} s per token; expert bytes drawn before timing)",
+            "seconds_per_token_layer": round(dt_all, 4),
+            "single_thread": {"value": round(bytes_step / dt_one / 1e9, 4), "unit": "GB/s", "threads": 1,
+                              "tokens": max(1, n_tokens // 3), "seconds_per_token_layer": round(dt_one, 4)}}
 
 
 def main():
@@ -428,7 +495,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--layers", type=int, default=8, help="layer instances the steps rotate over")
     ap.add_argument("--seed", type=int, default=0x5EED + 1)
-    ap.add_argument("--cpu-tokens", type=int, default=3)
+    ap.add_argument("--cpu-tokens", type=int, default=6)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--down-layout", choices=("mfma16", "tile256", "rows"), default="mfma16",
                     help="layout of the down projections (blocks permuted once at load time)")
@@ -469,11 +536,13 @@ def main():
         counter_pass(layers, x1, x8, ws, args.counter_pass)
         return
 
+    x1s = [torch.from_numpy(synth.token_bf16(15000 + i, 1, D).view(np.int16)).to("cuda") for i in range(16)]
+    x8s = [torch.from_numpy(synth.token_bf16(25000 + i, 8, D).view(np.int16)).to("cuda") for i in range(16)]
     log("timing B=1 ...")
-    ms1, wall1 = time_layer(layers, x1, 1, args.steps, args.warmup, ws)
+    ms1, wall1, settle1 = time_layer(layers, x1, 1, args.steps, args.warmup, ws, xs_settle=x1s)
     log("timing B=8 ...")
     idx_log = torch.empty((args.steps, 8, TOPK), dtype=torch.int32, device="cuda")
-    ms8, wall8 = time_layer(layers, x8, 8, args.steps, args.warmup, ws, idx_log)
+    ms8, wall8, settle8 = time_layer(layers, x8, 8, args.steps, args.warmup, ws, idx_log, x8s)
     uniq = [len(np.unique(r)) for r in idx_log.cpu().numpy()]
     U8 = float(np.mean(uniq))
     bytes1 = TOPK * 3 * MX_MAT + ROUTER
@@ -482,8 +551,11 @@ def main():
     gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
 
     log("per-kernel event timing ...")
-    k1s = profile_kernel(layers, x1, 1, args.steps, args.warmup, ws)
-    k8s = profile_kernel(layers, x8, 8, args.steps, args.warmup, ws)
+    nb = max(args.steps, 50)
+    xb1 = [torch.from_numpy(synth.token_bf16(35000 + i, 1, D).view(np.int16)).to("cuda") for i in range(nb)]
+    xb8 = [torch.from_numpy(synth.token_bf16(45000 + i, 8, D).view(np.int16)).to("cuda") for i in range(nb)]
+    k1s = profile_kernel(layers, xb1, 1, ws)
+    k8s = profile_kernel(layers, xb8, 8, ws)
     k1, k8 = float(np.mean(k1s)), float(np.mean(k8s))
 
     def spread(a):
@@ -519,7 +591,8 @@ def main():
         "b8": {"value": round(gbs8, 2), "unit": "GB/s", "ms_per_step": round(ms8, 5),
                "pct_hbm_peak": round(100 * gbs8 / HBM_PEAK_GBS, 2),
                "tokens_per_s_layer": round(8e3 / ms8, 1), "mean_unique_experts": round(U8, 2),
-               "bytes_per_step": round(bytes8)},
+               "bytes_per_step": round(bytes8), "host_wall_ms_per_step": round(wall8, 5), "settle": settle8},
+        "settle": settle1,
         "launch_bracket_ms": {"b1": round(k1, 5), "b8": round(k8, 5)},
         "launch_bracket_us_spread": {"b1": spread(k1s), "b8": spread(k8s)},
         "roofline": {"kernel": "fused_layer_kernel (MXFP4, B=1)", "bound": "hbm", "achieved": round(achieved, 2),
