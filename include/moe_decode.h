@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 enum moe_status {
   MOE_OK = 0,
@@ -54,7 +54,8 @@ enum moe_status {
   MOE_ERR_ARCH = 3,      /* the current HIP device is not gfx950 */
   MOE_ERR_HIP = 4,       /* a HIP call or kernel launch failed */
   MOE_ERR_WORKSPACE = 5, /* workspace missing, too small or not 256-byte aligned */
-  MOE_ERR_ALIGN = 6      /* a weight pointer or stride is not suitably aligned */
+  MOE_ERR_ALIGN = 6,     /* a weight pointer or stride is not suitably aligned */
+  MOE_ERR_SCRATCH = 7    /* moe_layer_decode_noalloc: the call needs more than the static scratch */
 };
 
 enum moe_format { MOE_FMT_MXFP4 = 0, MOE_FMT_Q2K = 1, MOE_FMT_INT4G32 = 2 };
@@ -239,6 +240,25 @@ int moe_layer_decode(const moe_layer_desc* L, const uint16_t* x_bf16, int B, flo
  * moe_layer_decode on a hash-routed layer returns MOE_ERR_ARG. */
 int moe_layer_decode_ids(const moe_layer_desc* L, const int32_t* token_ids, const uint16_t* x_bf16, int B,
                          float* y, void* ws, size_t ws_bytes, int32_t* idx_out, float* gw_out, void* stream);
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as moe_layer_decode, with the workspace taken from a static device
+ * array inside the library instead of a caller buffer.  The array holds
+ * MOE_STATIC_SCRATCH_BYTES per GPU (one copy on every device the library runs
+ * on, kept until the process ends), enough for every B <= 8 at the full layer
+ * shape (D 4096, F 2048, E 256, top_k 6); a call whose
+ * moe_layer_workspace_bytes(B, D, F, E, top_k) exceeds it returns
+ * MOE_ERR_SCRATCH before anything is enqueued.  It allocates and frees
+ * nothing.  The first call on a device looks the array up,
+ * clears it with a fill kernel on `stream` and synchronises `stream` once (do
+ * not make that first call under graph capture); later calls enqueue the
+ * layer only.  Every call on a GPU shares that GPU's array and leaves its
+ * contents for the next call, so calls that overlap on one GPU (different
+ * streams, or concurrent host threads) race and must be ordered by the
+ * caller.  Hash-routed layers are not supported (MOE_ERR_ARG). */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+int moe_layer_decode_noalloc(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, int32_t* idx_out,
+                             float* gw_out, void* stream);
 /* Sticky error flags of a layer or stack workspace, copied to the host
  * (synchronises `stream`): bit 0 a bounded wait gave up, bit 1 a hash-routed
  * layer met an invalid token id or table row.  They stay set until

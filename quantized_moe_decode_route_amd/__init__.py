@@ -20,7 +20,7 @@ FORMATS = {"mxfp4": MOE_FMT_MXFP4, "q2k": MOE_FMT_Q2K, "int4g32": MOE_FMT_INT4G3
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILE256, MOE_LAYOUT_MFMA16 = 0, 1, 2
 LAYOUTS = {"rows": MOE_LAYOUT_ROWS, "tile256": MOE_LAYOUT_TILE256, "mfma16": MOE_LAYOUT_MFMA16}
 # MOE_ABI_VERSION of include/moe_decode.h that this binding is written for
-ABI_VERSION = 6
+ABI_VERSION = 7
 MOE_MAX_TOKENS = 8
 MOE_MAX_TOPK = 8
 
@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_expert_gemv_mxfp4", "moe_expert_gemv_q2k", "moe_expert_gemv_int4g32",
     "moe_route_workspace_bytes", "moe_route_topk",
     "moe_layer_workspace_bytes", "moe_workspace_init", "moe_layer_decode", "moe_layer_decode_ids",
-    "moe_workspace_flags", "moe_layer_decode_profiled", "moe_layer_decode_traced",
+    "moe_layer_decode_noalloc", "moe_workspace_flags", "moe_layer_decode_profiled", "moe_layer_decode_traced",
     "moe_stack_workspace_bytes", "moe_stack_decode", "moe_stack_decode_ids", "moe_rmsnorm_bf16",
     "quantize_fp4_to_int4g32", "moe_validate_mxfp4", "moe_tile_weights", "moe_tile_weights_mfma16",
     "moe_q8k_quantize", "moe_expert_gemv_mxfp4_q8", "moe_mxfp4_half_lut", "moe_expert_gemv_mxfp4_hlut",
@@ -90,6 +90,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_decode": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _sz, _vp, _vp, _vp]),
             "moe_layer_decode_ids": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _vp, _i, _vp, _vp, _sz, _vp, _vp,
                                           _vp]),
+            "moe_layer_decode_noalloc": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _vp, _vp]),
             "moe_workspace_flags": (_i, [_vp, _sz, ctypes.POINTER(ctypes.c_uint32), _vp]),
             "moe_layer_decode_profiled": (_i, [ctypes.POINTER(moe_layer_desc), _vp, _i, _vp, _vp, _sz, _vp, _vp,
                                                ctypes.POINTER(_vp), _vp]),
@@ -251,6 +252,19 @@ def moe_layer_decode_ids(desc: moe_layer_desc, token_ids, x_bf16, y, ws, idx_out
            lib().moe_layer_decode_ids(ctypes.byref(desc), _ptr(token_ids), _ptr(x_bf16), B, _ptr(y), _ptr(ws),
                                       ws.numel() * ws.element_size(), _ptr(idx_out), _ptr(gw_out),
                                       _stream(stream)))
+
+
+MOE_ERR_SCRATCH = 7
+MOE_STATIC_SCRATCH_BYTES = 8 << 20
+
+
+def moe_layer_decode_noalloc(desc: moe_layer_desc, x_bf16, y, idx_out=None, gw_out=None, stream=None) -> None:
+    """moe_layer_decode with the library's static per-device scratch as the
+    workspace (for callers that cannot allocate)."""
+    B = x_bf16.shape[0]
+    _check("moe_layer_decode_noalloc",
+           lib().moe_layer_decode_noalloc(ctypes.byref(desc), _ptr(x_bf16), B, _ptr(y), _ptr(idx_out), _ptr(gw_out),
+                                          _stream(stream)))
 
 
 def moe_workspace_flags(ws, stream=None) -> int:

@@ -1,11 +1,20 @@
 // C ABI of libmoedecode: argument validation, workspace layout and launch
-// sequencing.  No entry point allocates device memory or synchronises.
+// sequencing.  No entry point allocates device memory; the few that
+// synchronise their stream once per device say so in the header.
 #include <hip/hip_runtime.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "moe_internal.h"
 
 using namespace moe;
+
+// Workspace of moe_layer_decode_noalloc: a file-scope device array, one copy
+// per GPU.  Host code never passes its name to a kernel (on the host the name
+// is a stand-in, not a device address); it uses the address
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -155,6 +164,34 @@ int layer_impl(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y,
   return MOE_OK;
 }
 
+// The current device's copy of `scratch`, set up on the first call on that
+// device: its address is looked up with that device current, and the array
+// is cleared (counters, epoch and exchange words must start at zero) with
+// the fill kernel; the stream is synchronised so that no later call on
+// another stream can overtake the clearing.
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_dev[64];
+
+int static_scratch(hipStream_t s, uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= 64) return MOE_ERR_ARG;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return hip_status(e);
+    if (!p || !aligned(p, 256)) return MOE_ERR_WORKSPACE;
+    static_assert(MOE_STATIC_SCRATCH_BYTES % 4 == 0 && MOE_STATIC_SCRATCH_BYTES / 4 < (1u << 30), "one fill launch");
+    if ((e = launch_zero_u32(static_cast<uint32_t*>(p), (int)(MOE_STATIC_SCRATCH_BYTES / 4), s)) != hipSuccess)
+      return hip_status(e);
+    if ((e = hipStreamSynchronize(s)) != hipSuccess) return hip_status(e);
+    g_scratch_dev[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return MOE_OK;
+}
+
 int check_ws(void* ws, size_t have, size_t need) {
   if (!ws) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return MOE_ERR_WORKSPACE;
@@ -190,6 +227,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_HIP: return "HIP runtime error (see moe_last_hip_error)";
     case MOE_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case MOE_ERR_ALIGN: return "pointer or stride misaligned";
+    case MOE_ERR_SCRATCH: return "the call needs more workspace than the library's static scratch holds";
     default: return "unknown status";
   }
 }
@@ -313,6 +351,22 @@ int moe_layer_decode(const moe_layer_desc* L, const uint16_t* x_bf16, int B, flo
 int moe_layer_decode_ids(const moe_layer_desc* L, const int32_t* token_ids, const uint16_t* x_bf16, int B, float* y,
                          void* ws, size_t ws_bytes, int32_t* idx_out, float* gw_out, void* stream) {
   return layer_entry(L, token_ids, x_bf16, B, y, ws, ws_bytes, idx_out, gw_out, nullptr, stream);
+}
+
+int moe_layer_decode_noalloc(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, int32_t* idx_out,
+                             float* gw_out, void* stream) {
+  int st = check_layer(L, B);
+  if (st != MOE_OK) return st;
+  if ((st = check_ids(L, nullptr)) != MOE_OK) return st;
+  if (!x_bf16 || !y) return MOE_ERR_ARG;
+  if (!aligned(x_bf16, 16) || !aligned(y, 16)) return MOE_ERR_ALIGN;
+  if (layer_ws_layout(B, L->d_model, L->d_ff, L->n_experts, L->top_k).total > MOE_STATIC_SCRATCH_BYTES)
+    return MOE_ERR_SCRATCH;
+  if ((st = arch_check()) != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = nullptr;
+  if ((st = static_scratch(s, &ws)) != MOE_OK) return st;
+  return layer_impl(L, x_bf16, B, y, nullptr, ws, idx_out, gw_out, nullptr, s);
 }
 
 int moe_workspace_flags(const void* ws, size_t ws_bytes, uint32_t* flags, void* stream) {

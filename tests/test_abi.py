@@ -47,8 +47,8 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert moe.moe_abi_version() == moe.ABI_VERSION == 6
-    for st in range(7):
+    assert moe.moe_abi_version() == moe.ABI_VERSION == 7
+    for st in range(8):
         assert moe.moe_status_string(st)
     assert moe.moe_status_string(0) == "ok"
 
@@ -160,6 +160,27 @@ def test_hash_routing_validation_on_host(L):
     f = ctypes.c_uint32(0)
     assert L.moe_workspace_flags(None, ws_ok, ctypes.byref(f), None) == 1
     assert L.moe_workspace_flags(FAKE + 16, ws_ok, ctypes.byref(f), None) == 5  # workspaces are 256-aligned
+
+
+def test_noalloc_validation_on_host(L):
+    """The static-scratch layer entry checks its arguments, and that the
+    call's workspace fits the static scratch, before touching the device."""
+    d = moe.make_layer_desc("mxfp4", FAKE, FAKE, FAKE, FAKE, 256, 4096, 2048, 6, 4456704, 4456704, 4456704)
+    N = L.moe_layer_decode_noalloc
+    assert N(None, FAKE, 1, FAKE, None, None, None) == 1
+    assert N(ctypes.byref(d), None, 1, FAKE, None, None, None) == 1
+    assert N(ctypes.byref(d), FAKE, 9, FAKE, None, None, None) == 2            # B > 8
+    assert N(ctypes.byref(d), FAKE + 8, 1, FAKE, None, None, None) == 6        # x 16-byte aligned
+    for B in range(1, 9):                                                      # the full shape fits at every B
+        assert moe.moe_layer_workspace_bytes(B, 4096, 2048, 256, 6) <= moe.MOE_STATIC_SCRATCH_BYTES
+    d.d_model = 8192                                                           # 12.4 MB at B = 8
+    assert moe.moe_layer_workspace_bytes(8, 8192, 2048, 256, 6) > moe.MOE_STATIC_SCRATCH_BYTES
+    assert N(ctypes.byref(d), FAKE, 8, FAKE, None, None, None) == moe.MOE_ERR_SCRATCH
+    h = moe.make_layer_desc("mxfp4", FAKE, FAKE, FAKE, FAKE, 256, 4096, 2048, 6, 4456704, 4456704, 4456704,
+                            tid2eid=FAKE, vocab=10)
+    assert N(ctypes.byref(h), FAKE, 1, FAKE, None, None, None) == 1            # hash routing needs ids
+    m = re.search(r"#define MOE_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == moe.MOE_STATIC_SCRATCH_BYTES
 
 
 def test_layout_validation_on_host(L):
