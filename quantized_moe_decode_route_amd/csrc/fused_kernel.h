@@ -287,9 +287,11 @@ static_assert(kHTerms <= kHCols && 16 % kHCols == 0, "a token's terms fit its co
 constexpr int kPrefetchExperts = 1;  // one token: experts whose gate/up rows go to L2 during top-k
 constexpr bool kPrefetchDown = true;  // ... and their down rows
 
-// F: format of gate and up; FD: format of down.
-template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD>
+// F: format of gate and up; FD: format of down.  ONE: built for one token
+// (B = 1 known at compile time; the in-kernel norm implies it).
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD, bool ONE = NORM>
 __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a) {
+  static_assert(!NORM || ONE, "the in-kernel norm is built for one token");
   constexpr int kCh = F::kXDw / 4;  // 16-byte chunks of one unit's staged activations
   constexpr int kRingGU = Rings<F>::kGU;
   constexpr int kRingDN = Rings<FD>::kDN;
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   const int g = blockIdx.x;
   const int w = threadIdx.x / kWave;
   const int lane = lane_id();
-  const int B = a.B, k = a.k, E = a.E, D = a.D, Fd = a.Fd;
+  const int B = ONE ? 1 : a.B, k = a.k, E = a.E, D = a.D, Fd = a.Fd;
   const int S = B * k;  // (token, rank) slots
   const uint64_t t_start = wall_clock64();  // trace slot 0, stored with slot 1 (no store this early)
   // The pointers of the first loads, fetched with the first group of scalar
@@ -1354,10 +1356,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   asm volatile("" ::"v"(nr_sink));  // the next layer's router line, long since arrived
 }
 
-template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD>
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD, bool ONE = NORM>
 hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK, NORM, FD>), dim3(grid), dim3(kW * kWave), 0,
-                     s, a);
+  if (ONE && a.B != 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK, NORM, FD, ONE>), dim3(grid),
+                     dim3(kW * kWave), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1367,6 +1370,10 @@ hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
 template <class F, int UPS, int DNK, bool NORM = false, class FD = F>
 hipError_t launch_fused_f(const FusedArgs& a, int grid, int gu_units, int dn_units, hipStream_t s) {
   if constexpr (DNK > 0) {
+    // the full layer shape (d_model > 2048, eight units per XCD slice) has a
+    // one-token build of its own
+    if constexpr (!NORM && UPS == 8)
+      if (gu_units > kWave && a.B == 1) return launch_fused_t<F, 2, 1, UPS, DNK, false, FD, true>(a, grid, s);
     return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, DNK, NORM, FD>(a, grid, s)
                             : launch_fused_t<F, 1, 1, UPS, DNK, NORM, FD>(a, grid, s);
   } else {
