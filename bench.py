@@ -340,6 +340,69 @@ def settle(launch, n_inputs: int) -> dict:
     return {"launches": n, "ms": round(ms, 2)}
 
 
+def stream_ceiling(layers, calls: int = 24):
+    """Pure-read rate of the device for the layer's load patterns
+    (moe_stream_read), over the resident layers' weight buffers (1.14 GB
+    each, far beyond the 256 MB last-level cache): 16-byte coalesced chunks
+    and 17-byte MXFP4 block windows.  GB/s counts the bytes of the range."""
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    bufs = [m for l in layers for m in l[1]]
+    sink = torch.zeros(moe.MOE_STREAM_GRID, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for pat in ("dwordx4", "mxfp4"):
+        nbytes = bufs[0].numel() - bufs[0].numel() % 16
+        for i in range(8):
+            moe.moe_stream_read(bufs[i % len(bufs)], nbytes, pat, sink, stream=s)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for i in range(calls):
+            moe.moe_stream_read(bufs[(i + 3) % len(bufs)], nbytes, pat, sink, stream=s)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / calls
+        out[pat] = {"GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_call": nbytes,
+                    "us_per_call": round(ms * 1e3, 2)}
+    return out
+
+
+def int4_conversion_leg(layers):
+    """quantize_fp4_to_int4g32 over one full layer: 768 MXFP4 matrices (256
+    experts x gate, up, down) in three calls, one per projection."""
+    import torch
+
+    import quantized_moe_decode_route_amd as moe
+    q = torch.empty(E * I4_Q, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(E * I4_S, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    mats = layers[0][1]
+    shapes = ((E * F, D), (E * F, D), (E * D, F))   # rows of all experts, columns
+
+    def one_layer():
+        for m, (n, k) in zip(mats, shapes):
+            moe.quantize_fp4_to_int4g32(m, n, k, q, sc, stream=s)
+    one_layer()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    start.record()
+    for _ in range(reps):
+        one_layer()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    bytes_in = 3 * E * MX_MAT
+    bytes_out = 3 * E * (I4_Q + I4_S)
+    del q, sc
+    torch.cuda.empty_cache()
+    return {"matrices": 3 * E, "ms_per_layer": round(ms, 3), "bytes_in": bytes_in, "bytes_out": bytes_out,
+            "GB/s": round((bytes_in + bytes_out) / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * (bytes_in + bytes_out) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+
+
 def time_layer(layers, xs, B, steps, warmup, ws, idx_log=None, xs_settle=None):
     """Average ms per step over `steps` layer launches (fresh token each, layer
     instances rotated), after a settle pass on other tokens and `warmup`
@@ -423,24 +486,34 @@ def numerics_pass(n):
     torch.cuda.synchronize()
 
 
-def counter_pass(layers, x1, x8, ws, n):
+def counter_pass(layers, x1, x8, ws, n, fmt="mxfp4"):
     """Fixed launch order for per-dispatch hardware counters: n B=1 layers,
-    n B=8 layers, n plain device copies of COPY_BYTES (known traffic)."""
+    n B=8 layers, n plain device copies of COPY_BYTES (known traffic).  The
+    experts the launches select are recorded, and each launch's algorithmic
+    bytes (its distinct experts' three projections once, plus the router)
+    are printed as one JSON line."""
     import torch
 
     import quantized_moe_decode_route_amd as moe
     nl = len(layers)
+    alg = {}
     for B, xs in ((1, x1), (8, x8)):
         y = torch.empty((B, D), dtype=torch.float32, device="cuda")
+        idx = torch.empty((n, B, TOPK), dtype=torch.int32, device="cuda")
         for i in range(n):
-            moe.moe_layer_decode(layers[i % nl][0], xs[i], y, ws)
+            moe.moe_layer_decode(layers[i % nl][0], xs[i], y, ws, idx[i])
         torch.cuda.synchronize()
+        check_flags(ws, f"counter pass B={B}")
+        U = [len(np.unique(r)) for r in idx.cpu().numpy()]
+        alg[f"b{B}"] = {"mean_unique_experts": round(float(np.mean(U)), 3),
+                        "bytes_per_launch": round(float(np.mean(U)) * EXPERT_BYTES[fmt] + ROUTER)}
     src = torch.zeros(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(n):
         torch.neg(src, out=dst)  # one elementwise kernel: reads and writes COPY_BYTES each
     torch.cuda.synchronize()
-    log(f"counter pass: {n} x B=1 layer, {n} x B=8 layer, {n} x elementwise copy of {COPY_BYTES} bytes")
+    log(f"counter pass ({fmt}): {n} x B=1 layer, {n} x B=8 layer, {n} x elementwise copy of {COPY_BYTES} bytes")
+    print(json.dumps({"counter_pass": fmt, "launches": n, "copy_bytes": COPY_BYTES, **alg}), flush=True)
 
 
 def cpu_baseline(seed: int, n_tokens: int):
@@ -506,6 +579,8 @@ def main():
                     help="instead of the benchmark: N B=1 layer launches, then N B=8 launches, then N "
                          "copies of a 256 MiB buffer (the copy calibrates HBM byte counters); for "
                          "rocprofv3 --pmc runs")
+    ap.add_argument("--counter-format", choices=("mxfp4", "q2k", "int4g32", "mxfp4+q2k"), default="mxfp4",
+                    help="weight format of the layers in --counter-pass")
     ap.add_argument("--numerics-pass", type=int, default=0, metavar="N",
                     help="instead of the benchmark: N launches each of the main, Q8 integer-dot and "
                          "binary16-table MXFP4 matvecs (W 2048 x 4096, B=8), for rocprofv3 --pmc runs")
@@ -524,8 +599,12 @@ def main():
     if args.numerics_pass:
         numerics_pass(args.numerics_pass)
         return
-    log(f"building {args.layers} MXFP4 layers ({args.layers * 3 * E * MX_MAT / 1e9:.1f} GB) ...")
-    layers = build_layers(args.layers, args.seed, args.down_layout)
+    if args.counter_pass and args.counter_format != "mxfp4":
+        log(f"building 4 {args.counter_format} layers ...")
+        layers = build_format_layers(args.counter_format, 4, args.seed + 7)
+    else:
+        log(f"building {args.layers} MXFP4 layers ({args.layers * 3 * E * MX_MAT / 1e9:.1f} GB) ...")
+        layers = build_layers(args.layers, args.seed, args.down_layout)
     n_tok = args.warmup + args.steps
     x1 = [torch.from_numpy(synth.token_bf16(10000 + i, 1, D).view(np.int16)).to("cuda") for i in range(n_tok)]
     x8 = [torch.from_numpy(synth.token_bf16(20000 + i, 8, D).view(np.int16)).to("cuda") for i in range(n_tok)]
@@ -533,7 +612,7 @@ def main():
     moe.moe_workspace_init(ws)
 
     if args.counter_pass:
-        counter_pass(layers, x1, x8, ws, args.counter_pass)
+        counter_pass(layers, x1, x8, ws, args.counter_pass, args.counter_format)
         return
 
     x1s = [torch.from_numpy(synth.token_bf16(15000 + i, 1, D).view(np.int16)).to("cuda") for i in range(16)]
@@ -550,6 +629,11 @@ def main():
     gbs1 = bytes1 / (ms1 * 1e-3) / 1e9
     gbs8 = bytes8 / (ms8 * 1e-3) / 1e9
 
+    log("streaming-read ceiling ...")
+    ceiling = stream_ceiling(layers)
+    ceil_mx = ceiling["mxfp4"]["GB/s"]
+    log("int4 conversion ...")
+    conv = int4_conversion_leg(layers)
     log("per-kernel event timing ...")
     nb = max(args.steps, 50)
     xb1 = [torch.from_numpy(synth.token_bf16(35000 + i, 1, D).view(np.int16)).to("cuda") for i in range(nb)]
@@ -585,11 +669,15 @@ def main():
                    "d_ff": F, "tokens_per_step": 1, "weight_format": "mxfp4",
                    "down_layout": args.down_layout, "layer_instances_rotated": args.layers},
         "pct_hbm_peak": round(100 * gbs1 / HBM_PEAK_GBS, 2),
+        "pct_of_measured_ceiling": round(100 * gbs1 / ceil_mx, 2),
+        "measured_read_ceiling": ceiling,
+        "int4_conversion": conv,
         "tokens_per_s_layer": round(1e3 / ms1, 1),
         "bytes_per_step": bytes1,
         "host_wall_ms_per_step": round(wall1, 5),
         "b8": {"value": round(gbs8, 2), "unit": "GB/s", "ms_per_step": round(ms8, 5),
                "pct_hbm_peak": round(100 * gbs8 / HBM_PEAK_GBS, 2),
+               "pct_of_measured_ceiling": round(100 * gbs8 / ceil_mx, 2),
                "tokens_per_s_layer": round(8e3 / ms8, 1), "mean_unique_experts": round(U8, 2),
                "bytes_per_step": round(bytes8), "host_wall_ms_per_step": round(wall8, 5), "settle": settle8},
         "settle": settle1,

@@ -309,6 +309,35 @@ int moe_stack_decode_ids(const moe_layer_desc* layers, int n_layers, const int32
 /* The norm step alone: x_out bfloat16 bits [B][D] from h fp32 [B][D]. */
 int moe_rmsnorm_bf16(const float* h, int B, int D, double eps, uint16_t* x_out, void* stream);
 
+/* ------------------------------------------------------------------ measurement
+ * A pure-read yardstick: the layer streams weights from HBM, so its
+ * effective bandwidth is compared with what a kernel doing nothing but reads
+ * achieves with the same load patterns ("Mixed-precision compression of
+ * DeepSeek-V4-Flash", "Capacity": measured pure-read bandwidth as the bound).
+ * moe_stream_read reads bytes [src, src + bytes) once and writes, per
+ * workgroup of its MOE_STREAM_GRID-workgroup launch, the XOR of every dword
+ * it loaded to sink[workgroup] (device uint32 [MOE_STREAM_GRID]); the XOR of
+ * all sink words is the XOR of the loaded dwords, which a test can check.
+ *   MOE_STREAM_DWORDX4: 16-byte chunks, consecutive lanes consecutive chunks
+ *     (src 16-byte aligned, bytes % 16 == 0; every dword is loaded once).
+ *   MOE_STREAM_MXFP4: the 17-byte blocks of an MXFP4 array loaded as the
+ *     matvecs do, the five dwords covering each block (src 4-byte aligned,
+ *     bytes % 4 == 0, bytes >= 20); blocks b = 0 .. moe_stream_mxfp4_blocks(bytes)-1
+ *     start at byte 17b, and the dwords from (17b & ~3) to (17b & ~3) + 16
+ *     are loaded (overlapping windows are loaded twice).
+ * Asynchronous on `stream`; MOE_ERR_ARG / _ALIGN / _SHAPE on bad arguments. */
+#define MOE_STREAM_GRID 2048
+enum moe_stream_pattern { MOE_STREAM_DWORDX4 = 0, MOE_STREAM_MXFP4 = 1 };
+int moe_stream_read(const void* src, size_t bytes, int pattern, uint32_t* sink, void* stream);
+/* Blocks the MXFP4 pattern reads in `bytes` bytes: the largest n whose last
+ * five-dword window ends inside the range (0 if bytes < 20). */
+static inline int64_t moe_stream_mxfp4_blocks(size_t bytes) {
+  if (bytes < 20) return 0;
+  int64_t n = (int64_t)(bytes / 17);
+  while (n > 0 && ((17 * (n - 1)) & ~(int64_t)3) + 20 > (int64_t)bytes) --n;
+  return n;
+}
+
 /* ------------------------------------------------------------------ FP4 -> INT4 g32
  * Per 32-weight group (= one MXFP4 block of a row): w_i = E2M1[c_i] *
  * 2^(e-127) in fp32; amax = max(max|w_i|, 1e-8); for r in {6/7, 0.9, 0.95,

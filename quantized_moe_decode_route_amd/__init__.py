@@ -33,6 +33,7 @@ EXPORTS = (
     "moe_stack_workspace_bytes", "moe_stack_decode", "moe_stack_decode_ids", "moe_rmsnorm_bf16",
     "quantize_fp4_to_int4g32", "moe_validate_mxfp4", "moe_tile_weights", "moe_tile_weights_mfma16",
     "moe_q8k_quantize", "moe_expert_gemv_mxfp4_q8", "moe_mxfp4_half_lut", "moe_expert_gemv_mxfp4_hlut",
+    "moe_stream_read",
 )
 
 
@@ -105,6 +106,7 @@ def lib() -> ctypes.CDLL:
             "moe_validate_mxfp4": (_i, [_vp, _i64, _vp, _vp]),
             "moe_tile_weights": (_i, [_i, _vp, _vp, _i, _i, _vp, _vp, _vp]),
             "moe_tile_weights_mfma16": (_i, [_vp, _i, _i, _vp, _vp]),
+            "moe_stream_read": (_i, [_vp, _sz, _i, _vp, _vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -355,3 +357,23 @@ def moe_tile_weights_mfma16(src, N: int, K: int, dst, stream=None) -> None:
 def moe_validate_mxfp4(blocks, n_blocks: int, bad_count_dev, stream=None) -> None:
     _check("moe_validate_mxfp4",
            lib().moe_validate_mxfp4(_ptr(blocks), n_blocks, _ptr(bad_count_dev), _stream(stream)))
+
+
+MOE_STREAM_GRID = 2048
+STREAM_PATTERNS = {"dwordx4": 0, "mxfp4": 1}
+
+
+def moe_stream_mxfp4_blocks(nbytes: int) -> int:
+    """Blocks the MXFP4 read pattern covers in ``nbytes`` bytes (as the header's inline function)."""
+    if nbytes < 20:
+        return 0
+    n = nbytes // 17
+    while n > 0 and ((17 * (n - 1)) & ~3) + 20 > nbytes:
+        n -= 1
+    return n
+
+
+def moe_stream_read(src, nbytes: int, pattern: str, sink, stream=None) -> None:
+    """Pure-read probe: one XOR of the loaded dwords per workgroup into ``sink`` (uint32 [MOE_STREAM_GRID])."""
+    _check("moe_stream_read",
+           lib().moe_stream_read(_ptr(src), nbytes, STREAM_PATTERNS[pattern], _ptr(sink), _stream(stream)))

@@ -506,6 +506,18 @@ int moe_tile_weights_mfma16(const uint8_t* src, int N, int K, uint8_t* dst, void
   return hip_status(launch_tile_mfma16(src, dst, N, K, (hipStream_t)stream));
 }
 
+int moe_stream_read(const void* src, size_t bytes, int pattern, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes == 0) return MOE_ERR_ARG;
+  if (pattern != MOE_STREAM_DWORDX4 && pattern != MOE_STREAM_MXFP4) return MOE_ERR_ARG;
+  if (pattern == MOE_STREAM_DWORDX4 ? (!aligned(src, 16) || bytes % 16) : (!aligned(src, 4) || bytes % 4))
+    return MOE_ERR_ALIGN;
+  if (pattern == MOE_STREAM_MXFP4 && bytes < 20) return MOE_ERR_SHAPE;
+  if (!aligned(sink, 4)) return MOE_ERR_ALIGN;
+  int st = arch_check();
+  if (st != MOE_OK) return st;
+  return hip_status(launch_stream_read(src, (int64_t)bytes, pattern, sink, (hipStream_t)stream));
+}
+
 int moe_validate_mxfp4(const uint8_t* blocks, int64_t n_blocks, int32_t* bad_count_dev, void* stream) {
   if (!blocks || !bad_count_dev || n_blocks < 0) return MOE_ERR_ARG;
   int st = arch_check();

@@ -353,6 +353,10 @@ hipError_t launch_validate_mxfp4(const uint8_t* blocks, int64_t n, int32_t* bad,
 
 hipError_t launch_zero_u32(uint32_t* p, int n, hipStream_t s);
 
+// Pure-read probe (stream.hip): reads [src, src + bytes) with pattern
+// (enum moe_stream_pattern), one XOR per workgroup into sink[MOE_STREAM_GRID].
+hipError_t launch_stream_read(const void* src, int64_t bytes, int pattern, uint32_t* sink, hipStream_t s);
+
 // dst[(c*N + n)*tile + i] = src[n*tiles*tile + c*tile + i] for c < tiles,
 // n < N, i < tile (elements of 2 or 4 bytes).
 hipError_t launch_tile_rows(const void* src, void* dst, int64_t N, int tiles, int tile_elems, int elem_bytes,

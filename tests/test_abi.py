@@ -117,6 +117,13 @@ def test_layer_and_route_validation_on_host(L):
     assert L.quantize_fp4_to_int4g32(FAKE, 8, 48, FAKE, FAKE, None) == 2
     assert L.quantize_fp4_to_int4g32(FAKE, 8, 64, FAKE + 4, FAKE, None) == 6
     assert L.moe_validate_mxfp4(FAKE, -1, FAKE, None) == 1
+    S = L.moe_stream_read
+    assert S(None, 64, 0, FAKE, None) == 1 and S(FAKE, 0, 0, FAKE, None) == 1
+    assert S(FAKE, 64, 2, FAKE, None) == 1                 # not a pattern
+    assert S(FAKE + 4, 64, 0, FAKE, None) == 6 and S(FAKE, 40, 0, FAKE, None) == 6
+    assert S(FAKE + 2, 64, 1, FAKE, None) == 6 and S(FAKE, 16, 1, FAKE, None) == 2
+    assert moe.moe_stream_mxfp4_blocks(19) == 0 and moe.moe_stream_mxfp4_blocks(20) == 1
+    assert moe.moe_stream_mxfp4_blocks(17 * 128) == 128     # one 4096-column MXFP4 row
 
 
 def test_mixed_format_validation_on_host(L):
