@@ -16,7 +16,8 @@ namespace {
 
 // acc[r] = dot of row r with one token's activation x, over the whole row.
 // Tokens that share rows call this once each; the repeated reads of the same
-// rows by the same wave are served by the caches.
+// rows by the same wave are served by the caches (the stand-alone matvec
+// keeps short rows in registers instead: gemv_regs_kernel).
 template <class F, int R>
 __device__ __forceinline__ void rows_dot(const typename F::Row (&rows)[R], int K, const float* __restrict__ x,
                                          float (&acc)[R]) {
@@ -103,6 +104,110 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ w
         if (row0 + r < N) y[(int64_t)t * N + row0 + r] = acc[r];
     }
   }
+}
+
+// The same matvec with the wave's weights held in registers: every lane
+// first requests all of its units of the kGemvR rows (UPL units per row, one
+// memory round trip), then each token's dots run from those registers, so
+// the weights are loaded once whatever B is.  The workgroup stages the
+// activations of as many tokens as fit in LDS (64 KB) at a time, so a
+// token's dots wait for LDS rather than for one L2 round trip per token.
+// The per-token arithmetic is rows_dot's (a lane adds its units in ascending
+// order, then the wave sums), so the results are the same bits.
+constexpr int kGemvXs = 16384;  // fp32 activations staged per chunk of tokens
+
+template <class F, int UPL>
+__global__ __launch_bounds__(256) void gemv_regs_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ sc,
+                                                        int N, int K, const float* __restrict__ x, int B,
+                                                        float* __restrict__ y) {
+  __shared__ __align__(16) float xs[kGemvXs];
+  const int wave = threadIdx.x / kWave;
+  const int row0 = (blockIdx.x * 4 + wave) * kGemvR;
+  const bool rows_here = row0 < N;  // waves without rows still stage activations
+  const int U = F::units(K);
+  const int lane = lane_id();
+  typename F::Raw raw[kGemvR][UPL];
+#pragma unroll
+  for (int r = 0; r < kGemvR; ++r) {
+    const typename F::Row row = F::row(w, sc, min(min(row0, N - 1) + r, N - 1), K);
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) {
+      const int u = lane + kWave * i;
+      F::load(row, u < U ? u : 0, raw[r][i]);
+    }
+  }
+  const int tc = K <= kGemvXs ? kGemvXs / K : 0;  // tokens per chunk (0: read x from memory)
+  for (int t0 = 0; t0 < B; t0 += tc > 0 ? tc : B) {
+    const int nt = tc > 0 ? min(tc, B - t0) : B;
+    if (tc > 0) {
+      __syncthreads();  // the previous chunk is consumed
+      const float4* src = reinterpret_cast<const float4*>(x + (int64_t)t0 * K);
+      // chunk c (4 activations) of unit u of token t goes to float4 slot
+      // t * K/4 + c * U + u: the lanes' reads of one chunk are consecutive
+      constexpr int C = F::kUnitW / 4;
+      const int K4 = K / 4;
+      for (int i = threadIdx.x; i < nt * K4; i += blockDim.x) {
+        const int t = i / K4, j = i - t * K4;
+        reinterpret_cast<float4*>(xs)[t * K4 + (j % C) * U + j / C] = src[i];
+      }
+      __syncthreads();
+    }
+    if (!rows_here) continue;
+    for (int t = t0; t < t0 + nt; ++t) {
+      float acc[kGemvR];
+#pragma unroll
+      for (int r = 0; r < kGemvR; ++r) acc[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < UPL; ++i) {
+        const int u = lane + kWave * i;
+        if (u < U) {
+          if (tc > 0) {
+            constexpr int C = F::kUnitW / 4;
+            const float4* xt4 = reinterpret_cast<const float4*>(xs) + (t - t0) * (K / 4) + u;
+            float xv[F::kUnitW];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+              const float4 v = xt4[c * U];
+              xv[4 * c] = v.x;
+              xv[4 * c + 1] = v.y;
+              xv[4 * c + 2] = v.z;
+              xv[4 * c + 3] = v.w;
+            }
+#pragma unroll
+            for (int r = 0; r < kGemvR; ++r) acc[r] += F::dot(raw[r][i], (uint32_t)u & 3u, xv);
+          } else {
+            const float* xt = x + (int64_t)t * K + (int64_t)F::kUnitW * u;
+#pragma unroll
+            for (int r = 0; r < kGemvR; ++r) acc[r] += F::dot(raw[r][i], (uint32_t)u & 3u, xt);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kGemvR; ++r) acc[r] = wave_sum(acc[r]);
+      if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < kGemvR; ++r)
+          if (row0 + r < N) y[(int64_t)t * N + row0 + r] = acc[r];
+      }
+    }
+  }
+}
+
+template <class F>
+hipError_t launch_gemv_f(const uint8_t* w, const uint16_t* scale, int N, int K, const float* x, int B, float* y,
+                         hipStream_t s) {
+  const int rows_per_block = 4 * kGemvR;
+  const dim3 grid((N + rows_per_block - 1) / rows_per_block);
+  const int upl = (K / F::kUnitW + kWave - 1) / kWave;  // units per lane and row
+  if (upl <= 1)
+    hipLaunchKernelGGL((gemv_regs_kernel<F, 1>), grid, dim3(256), 0, s, w, scale, N, K, x, B, y);
+  else if (upl <= 2)
+    hipLaunchKernelGGL((gemv_regs_kernel<F, 2>), grid, dim3(256), 0, s, w, scale, N, K, x, B, y);
+  else if (upl <= 4)
+    hipLaunchKernelGGL((gemv_regs_kernel<F, 4>), grid, dim3(256), 0, s, w, scale, N, K, x, B, y);
+  else  // long rows: stream them per token
+    hipLaunchKernelGGL(gemv_kernel<F>, grid, dim3(256), 0, s, w, scale, N, K, x, B, y);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- layer phases
@@ -212,10 +317,13 @@ __global__ __launch_bounds__(256) void down_kernel(WeightRef down, int D, int Fd
 
 hipError_t launch_gemv(int fmt, const void* w0, const uint16_t* scale, int N, int K, const float* x, int B,
                        float* y, hipStream_t s) {
-  const int rows_per_block = 4 * kGemvR;
-  dim3 grid((N + rows_per_block - 1) / rows_per_block);
   const uint8_t* w = static_cast<const uint8_t*>(w0);
-  MOE_DISPATCH(gemv_kernel, grid, s, w, scale, N, K, x, B, y)
+  switch (fmt) {
+    case MOE_FMT_MXFP4: return launch_gemv_f<MxFmt>(w, scale, N, K, x, B, y, s);
+    case MOE_FMT_Q2K: return launch_gemv_f<Q2kFmt>(w, scale, N, K, x, B, y, s);
+    case MOE_FMT_INT4G32: return launch_gemv_f<Int4Fmt>(w, scale, N, K, x, B, y, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gate_up(int fmt, const WeightRef& gate, const WeightRef& up, int D, int F, int B, int k,
