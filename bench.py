@@ -712,7 +712,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "mxfp4*bf16->fp32",
+        "numerics": {"weights": "mxfp4 (E2M1 codes, E8M0 scale per 32)", "x": "bf16", "router": "fp32 weights, fp64 sums",
+                     "accumulate": "fp32", "h": "fp32, entering the down MFMA as six base-16 E4M3 digit terms"},
         "data": "synthetic",
         "config": {"workload": "moe_layer_decode_mxfp4_b1", "experts": E, "top_k": TOPK, "d_model": D,
                    "d_ff": F, "tokens_per_step": 1, "weight_format": "mxfp4",
