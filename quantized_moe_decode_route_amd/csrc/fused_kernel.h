@@ -58,6 +58,12 @@ __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 
 __device__ __forceinline__ uint32_t payload_of(uint64_t w) { return (uint32_t)w; }
 
 // device-wide (agent-coherent)
+// A global-memory pointer from its integer value (through an address-space
+// cast, so that the compiler keeps its accesses global ones).
+template <class T>
+__device__ __forceinline__ T* as_global(uint64_t v) {
+  return (T*)(__attribute__((address_space(1))) T*)v;
+}
 __device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -207,8 +213,10 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xFu;  // HW_REG_XCC_ID bits 3:0
 }
 
-__device__ __forceinline__ void stamp(const FusedArgs& a, int point, unsigned by_thread = 0) {
-  if (a.trace && threadIdx.x == by_thread) a.trace[blockIdx.x * kTracePoints + point] = wall_clock64();
+// Trace records are kept in LDS (thread 0's stamps) and written out once at
+// the end, so a stamp costs no global store (and no wait for one).
+__device__ __forceinline__ void stamp(bool traced, uint64_t* rec, int point) {
+  if (traced && threadIdx.x == 0) rec[point] = wall_clock64();
 }
 
 // Marks every dword of a ring slot as used here, on every path: the wave
@@ -295,24 +303,61 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   constexpr int kCh = F::kXDw / 4;  // 16-byte chunks of one unit's staged activations
   constexpr int kRingGU = Rings<F>::kGU;
   constexpr int kRingDN = Rings<FD>::kDN;
-  const int G = gridDim.x;
   const int g = blockIdx.x;
   const int w = threadIdx.x / kWave;
   const int lane = lane_id();
-  const int B = ONE ? 1 : a.B, k = a.k, E = a.E, D = a.D, Fd = a.Fd;
+  // The scalars of the routing phase, requested as one group of scalar loads
+  // (one wait) and then held in registers: passing them through an empty asm
+  // keeps the compiler from reloading them from the argument buffer later,
+  // where each reload would also wait for the epoch load below (scalar loads
+  // retire out of order, so a wait for one is a wait for all).
+  // (Pointers pass as integers and come back as global-memory pointers, so
+  // their loads and stores stay global ones.)
+  uint64_t router_i = (uint64_t)a.router_w, x_i = (uint64_t)a.x, h_i = (uint64_t)a.hn, ws_i = (uint64_t)a.ws;
+  uint64_t ctr_off = a.L.counters, lg_off = a.L.logit_tags, trace_i = (uint64_t)a.trace;
+  int G = gridDim.x, NX = a.nx, E = a.E, D = a.D, Bv = a.B, k = a.k;
+  asm volatile("" : "+s"(router_i), "+s"(x_i), "+s"(h_i), "+s"(ws_i), "+s"(ctr_off), "+s"(lg_off), "+s"(trace_i));
+  asm volatile("" : "+s"(G), "+s"(NX), "+s"(E), "+s"(D), "+s"(Bv), "+s"(k));
+  const float* router_w = as_global<const float>(router_i);
+  const uint16_t* x_in = as_global<const uint16_t>(x_i);
+  const float* h_in = as_global<const float>(h_i);
+  uint8_t* ws = as_global<uint8_t>(ws_i);
+  const bool traced = trace_i != 0u;
+  const int B = ONE ? 1 : Bv, Fd = a.Fd;
   const int S = B * k;  // (token, rank) slots
-  const uint64_t t_start = wall_clock64();  // trace slot 0, stored with slot 1 (no store this early)
-  // The pointers of the first loads, fetched with the first group of scalar
-  // loads (otherwise the compiler may fetch them after the LDS set-up).
-  asm volatile("" ::"s"(a.router_w), "s"(NORM ? (const void*)a.hn : (const void*)a.x));
-  uint32_t* ctr = reinterpret_cast<uint32_t*>(a.ws + a.L.counters);
+  const uint64_t t_start = wall_clock64();  // trace slot 0 (kept in a register until the LDS record is set up)
+  // First requests: this thread's 8-element chunk of the workgroup's router
+  // row and of the activations (x, or h for the in-kernel norm), issued
+  // unconditionally (clamped to a valid row and chunk) before the call's
+  // epoch and the XCD counter are requested.
+  const int c8 = min(8 * (int)threadIdx.x, D - 8);
+  float4 fha, fhb;       // the in-kernel norm: h chunk (requested before the router row)
+  if constexpr (NORM) {
+    fha = *reinterpret_cast<const float4*>(h_in + c8);
+    fhb = *reinterpret_cast<const float4*>(h_in + c8 + 4);
+  }
+  const float* frow = router_w + (int64_t)min(g, E - 1) * D + c8;
+  const float4 fw0 = *reinterpret_cast<const float4*>(frow);
+  const float4 fw1 = *reinterpret_cast<const float4*>(frow + 4);
+  uint4 fx[kMaxTok];  // x chunks of every token (rows past B - 1 repeat the last one)
+  if constexpr (!NORM) {
+#pragma unroll
+    for (int t = 0; t < kMaxTok; ++t) fx[t] = *reinterpret_cast<const uint4*>(x_in + (int64_t)min(t, B - 1) * D + c8);
+  }
+  uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + ctr_off);
   // This call's epoch, read with a scalar load: a vector load here would
   // make the first use of the tag wait for the x and atomic requests issued
-  // after it.  (Workgroup 0 advances the counter only after every workgroup
-  // has read it.)
+  // after it.  Its first use is deferred to the first publication (the asm
+  // in tag_now), so the scalar waits before it do not include this load.
+  // (Workgroup 0 advances the counter only after every workgroup has read it.)
   typedef const __attribute__((address_space(4))) uint32_t ConstU32;
-  uint32_t tag = ((ConstU32*)ctr)[kCtrEpoch] + 1u;
-  if (tag == 0u) tag = 1u;              // tags start at 1 (the workspace starts zeroed)
+  uint32_t epoch = ((ConstU32*)ctr)[kCtrEpoch];
+  uint32_t tag = 0u;
+  auto tag_now = [&]() {
+    asm volatile("" : "+s"(epoch));
+    tag = epoch + 1u;
+    if (tag == 0u) tag = 1u;  // tags start at 1 (the workspace starts zeroed)
+  };
 
   __shared__ int32_t s_idx[kMaxSlots];
   __shared__ float s_gw[kMaxSlots];
@@ -326,9 +371,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   __shared__ int s_pre_n;                // ... and how many are known
   __shared__ int s_timeout;
   __shared__ int s_jx;
+  __shared__ uint64_t s_trace[kTracePoints];  // this workgroup's trace record (traced calls)
   __shared__ __align__(16) uint8_t s_buf[kLdsBytes];
 
-  const int NX = a.nx;
   const int xcd = (int)xcc_id();
   const int GX = G / NX;  // workgroups per XCD
   // Index inside the XCD: every call adds exactly GX to each XCD's counter.
@@ -337,6 +382,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   uint32_t xcd_arrival = 0;
   int trace_rereads = 0;  // thread 0: re-read passes of the logit (low half) and h (high half) waits
   if (threadIdx.x == 0) s_timeout = 0;
+  if (traced && threadIdx.x < kTracePoints) s_trace[threadIdx.x] = 0ull;  // slots a path does not stamp read 0
   // Requested right after this thread's first router loads (its result is
   // needed only after the logits), so nothing waits for it before them.
   bool arrival_pending = true;
@@ -345,7 +391,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       xcd_arrival = __hip_atomic_fetch_add(ctr + kCtrXcdBase + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     arrival_pending = false;
   };
-  for (int i = threadIdx.x; i < MOE_MAX_EXPERTS; i += blockDim.x) s_mask[i] = 0u;
+  static_assert(MOE_MAX_EXPERTS <= kW * kWave, "one expert word per thread");
+  if (threadIdx.x < MOE_MAX_EXPERTS) s_mask[threadIdx.x] = 0u;
   if (threadIdx.x == 0) {
     s_next = 0;
     s_gu_next = 0;
@@ -362,7 +409,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // (The LDS words cleared above are next used after the logits' barriers.)
 
   // ---------------------------------------------------------------- 1. routing
-  uint64_t* lg = reinterpret_cast<uint64_t*>(a.ws + a.L.logit_tags);  // [B][E][2]: high, low halves
+  uint64_t* lg = reinterpret_cast<uint64_t*>(ws + lg_off);  // [B][E][2]: high, low halves
   // Router logit partial sums over one 8-element chunk of every token.
   auto dot8 = [&](double (&acc)[kMaxTok], const float4& w0, const float4& w1, const uint4 (&xall)[kMaxTok]) {
 #pragma unroll
@@ -390,6 +437,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       }
     }
     __syncthreads();
+    tag_now();
     // The last wave publishes (at B < 8 it gathers no token, so the other
     // waves' reads of the logits do not wait behind these stores).
     if (threadIdx.x >= (kW - 1) * kWave && threadIdx.x < (kW - 1) * kWave + B) {
@@ -411,13 +459,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     // LDS for gate/up (F::stage8).
     // The loads are issued unconditionally (clamped to valid rows), h first:
     // the norm then waits for h alone while the router row is in flight.
-    const bool mine = 8 * (int)threadIdx.x < D;
-    const int c8 = mine ? 8 * (int)threadIdx.x : 0;
-    float4 ha = *reinterpret_cast<const float4*>(a.hn + c8);
-    float4 hb = *reinterpret_cast<const float4*>(a.hn + c8 + 4);
-    const float* row0 = a.router_w + (int64_t)min(g, E - 1) * D + c8;
-    float4 w0 = *reinterpret_cast<const float4*>(row0);
-    float4 w1 = *reinterpret_cast<const float4*>(row0 + 4);
+    const bool mine = 8 * (int)threadIdx.x < D;  // then c8 = 8 * threadIdx.x
+    float4 ha = fha, hb = fhb, w0 = fw0, w1 = fw1;
     take_arrival();
     if (!mine) ha = hb = make_float4(0.f, 0.f, 0.f, 0.f);
     const double ss = wave_sum_dpp_f64(rms_squares8(ha, hb, 0.0));
@@ -433,7 +476,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     for (int t = 0; t < kMaxTok; ++t) xall[t] = xn;
     for (int e = g; e < E; e += G) {
       if (e != g) {
-        const float* row = a.router_w + (int64_t)e * D + c8;
+        const float* row = router_w + (int64_t)e * D + c8;
         w0 = *reinterpret_cast<const float4*>(row);
         w1 = *reinterpret_cast<const float4*>(row + 4);
       }
@@ -446,7 +489,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   } else {
     uint4 xkeep[kMaxTok];  // this thread's x chunks of the first router row, for the staging
     for (int e = g; e < E; e += G) {
-      const float* row = a.router_w + (int64_t)e * D;
+      const float* row = router_w + (int64_t)e * D;
       double acc[kMaxTok];
 #pragma unroll
       for (int t = 0; t < kMaxTok; ++t) acc[t] = 0.0;
@@ -456,7 +499,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         uint4 xall[kMaxTok];  // every token's activations requested before the first use
 #pragma unroll
         for (int t = 0; t < kMaxTok; ++t)
-          xall[t] = *reinterpret_cast<const uint4*>(a.x + (int64_t)min(t, B - 1) * D + c);
+          xall[t] = *reinterpret_cast<const uint4*>(x_in + (int64_t)min(t, B - 1) * D + c);
         take_arrival();
         dot8(acc, w0, w1, xall);
         if (e == g) {
@@ -467,7 +510,16 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       // One 8-weight chunk per thread in straight-line code when the row
       // fits (d_model <= 4096): no loop header for the compiler to wait at.
       if (D <= 8 * kW * kWave) {
-        if (8 * (int)threadIdx.x < D) chunk(8 * threadIdx.x);
+        if (e == g) {  // the chunk requested first
+          if (8 * (int)threadIdx.x < D) {
+            take_arrival();
+            dot8(acc, fw0, fw1, fx);
+#pragma unroll
+            for (int t = 0; t < kMaxTok; ++t) xkeep[t] = fx[t];
+          }
+        } else if (8 * (int)threadIdx.x < D) {
+          chunk(8 * threadIdx.x);
+        }
       } else {
         for (int c = 8 * threadIdx.x; c < D; c += 8 * kW * kWave) chunk(c);
       }
@@ -480,20 +532,21 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
   }
   take_arrival();  // workgroups without a router row
-  if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints] = t_start;
-  stamp(a, 1);
+  tag_now();
+  if (traced && threadIdx.x == 0) s_trace[0] = t_start;
+  stamp(traced, s_trace, 1);
   // Activations for gate/up of a workgroup that has not staged them above
   // (no router row): requested now, staged in LDS ([t][chunk][unit], so
   // lanes read consecutive chunks) after the routing, which hides their
-  // latency.  B * units <= 2 * blockDim for every shape this kernel accepts.
+  // latency.  B * units <= 2 * (kW * kWave) for every shape this kernel accepts.
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int i = threadIdx.x + q * kW * kWave;
     if (!early_x && i < B * UG) {
-      F::load_x(a.x + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);  // (never with NORM: staged above)
+      F::load_x(x_in + (int64_t)(i / UG) * D, i - (i / UG) * UG, xraw[q]);  // (never with NORM: staged above)
     }
   }
-  stamp(a, 2);
+  stamp(traced, s_trace, 2);
 
   // Gather every logit (all reads issued before the first wait), then top-k:
   // wave t handles token t.  Each lane sorts its four candidates; every round
@@ -514,8 +567,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       wv[0] = lane < k ? ld_dev(p) : 0ull;
       wv[1] = lane < k ? ld_dev(p + 1) : 0ull;
       const int rr = await_tags<2>([&](int j) { return p + j; }, wv, valid, tag, wall_clock64(), &s_timeout);
-      if (a.trace && threadIdx.x == 0) trace_rereads = rr;
-      if (t == 0) stamp(a, 3);
+      if (traced && threadIdx.x == 0) trace_rereads = rr;
+      if (t == 0) stamp(traced, s_trace, 3);
       if (lane < k) my_v = __hiloint2double((int)payload_of(wv[0]), (int)payload_of(wv[1]));
       if (B == 1) {  // for the prefetching waves
         if (lane < k) lds_put(&s_pre[lane], my_i);
@@ -546,14 +599,14 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         const int rr = await_tags<2 * kPer>(
             [&](int j) { return lg + ((int64_t)t * E + lane + kWave * (j >> 1)) * 2 + (j & 1); }, wv, valid, tag,
             wall_clock64(), &s_timeout);
-        if (a.trace && threadIdx.x == 0) trace_rereads = rr;
+        if (traced && threadIdx.x == 0) trace_rereads = rr;
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
           hw[i] = wv[2 * i];
           lw[i] = wv[2 * i + 1];
         }
       }
-      if (t == 0) stamp(a, 3);
+      if (t == 0) stamp(traced, s_trace, 3);
       double v[kPer];
       int id[kPer];
 #pragma unroll
@@ -644,9 +697,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
   if (threadIdx.x == 0) {  // the arrival counter has long returned by now
     s_jx = (int)(xcd_arrival % (uint32_t)GX);
-    if (a.trace) {
-      a.trace[blockIdx.x * kTracePoints + kTracePoints - 2] = (uint64_t)xcd;
-      a.trace[blockIdx.x * kTracePoints + kTracePoints - 1] = (uint64_t)xcd_arrival;
+    if (traced) {
+      s_trace[kTracePoints - 2] = (uint64_t)xcd;
+      s_trace[kTracePoints - 1] = (uint64_t)xcd_arrival;
     }
   }
   // Stage the activations requested above (their loads have long returned:
@@ -725,7 +778,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
   }
   __syncthreads();
-  stamp(a, 4);
+  stamp(traced, s_trace, 4);
   // Group (token, rank) pairs by expert, experts ascending: one record per
   // selected expert holding its packed token mask.  Every wave builds the
   // table itself (in its own LDS row, read back by the same wave), so no
@@ -773,12 +826,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   auto grp_expert = [&](int uu) { return __builtin_amdgcn_readlane(g_exp, uu); };
   auto grp_mask = [&](int uu) { return (uint32_t)__builtin_amdgcn_readlane((int)g_mask, uu); };
   if (g == 0) {
-    for (int i = threadIdx.x; i < S; i += blockDim.x) {
+    for (int i = threadIdx.x; i < S; i += kW * kWave) {
       if (a.idx_out) a.idx_out[i] = s_idx[i];
       if (a.gw_out) a.gw_out[i] = s_gw[i];
     }
   }
-  stamp(a, 5);
+  stamp(traced, s_trace, 5);
 
   // ---------------------------------------------------------------- 2. gate / up
   const int jx = s_jx;     // index inside the XCD
@@ -1203,7 +1256,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     // every later slot is dead too
     while (item[kRingGU - 1] < NI) pass(std::false_type{});
   }
-  stamp(a, 6);
+  stamp(traced, s_trace, 6);
 #pragma unroll
   for (int r = 0; r < kPrefetchExperts; ++r) asm volatile("" ::"v"(pre_sink[r]));  // long since arrived
   fill_slot_tables();
@@ -1218,7 +1271,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // ---------------------------------------------------------------- 3. down (partials over the slice)
   if constexpr (DNK == 0) {
   __syncthreads();  // the activation view of s_buf is no longer used
-  stamp(a, 11);
+  stamp(traced, s_trace, 11);
   {
     // Gather this XCD's h slice for every slot (written by the XCD's workgroups).
     const int g_first = threadIdx.x, g_step = kW * kWave;
@@ -1247,8 +1300,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         }
       }
     }
-    stamp(a, 12);
-    if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints + 13] = (uint64_t)trace_rereads;
+    stamp(traced, s_trace, 12);
+    if (traced && threadIdx.x == 0) s_trace[13] = (uint64_t)trace_rereads;
     __syncthreads();
     if (FD::kPrepH) {
       for (int i = threadIdx.x; i < S * UPS; i += kW * kWave) FD::prep_h(sh + i * kHB);
@@ -1258,7 +1311,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
   if constexpr (DNK > 0) {
     __syncthreads();  // every row of this workgroup is published; the activations are dead
-    stamp(a, 11);
+    stamp(traced, s_trace, 11);
     // the zero B operand and exponents (slot S), read by lanes without a token or term
     for (int i = threadIdx.x; i < kHbSlot / 16; i += kW * kWave)
       reinterpret_cast<uint4*>(hb + (size_t)S * kHbSlot)[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -1270,11 +1323,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       while (gather_batch(std::integral_constant<int, 3>{})) {
       }
     }
-    stamp(a, 12);
-    if (a.trace && threadIdx.x == 0) a.trace[blockIdx.x * kTracePoints + 13] = (uint64_t)trace_rereads;
+    stamp(traced, s_trace, 12);
+    if (traced && threadIdx.x == 0) s_trace[13] = (uint64_t)trace_rereads;
     __syncthreads();
   }
-  stamp(a, 7);
+  stamp(traced, s_trace, 7);
   if (DNK > 0 && dn_walk && B <= 16 / kHCols && dn_full) {
     // Every group's down weights are in the prologue slots and every group
     // has at most two tokens (one MFMA pass): the groups are computed in
@@ -1299,7 +1352,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
   }
   __syncthreads();
-  stamp(a, 8);
+  stamp(traced, s_trace, 8);
   // Combine the k ranks in rank order and publish this XCD's partial rows
   // (first half of the waves), while the second half gathers the partials of
   // the rows this workgroup finishes.
@@ -1315,7 +1368,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       }
     }
   }
-  stamp(a, 9);
+  stamp(traced, s_trace, 9);
 
   // ---------------------------------------------------------------- finish: sum the NX partials
   if (w >= kW / 2) {
@@ -1346,7 +1399,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
   }
   __syncthreads();
-  stamp(a, 10);
+  stamp(traced, s_trace, 10);
+  if (a.trace && threadIdx.x < kTracePoints) a.trace[blockIdx.x * kTracePoints + threadIdx.x] = s_trace[threadIdx.x];
   if (threadIdx.x == 0) {
     if (s_timeout) __hip_atomic_fetch_or(ctr + kCtrTimeout, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // Every workgroup has read the epoch before workgroup 0 gets here
