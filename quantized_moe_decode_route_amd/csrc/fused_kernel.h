@@ -634,43 +634,46 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       cswap(0, 2);
       cswap(1, 3);
       cswap(1, 2);
+      uint32_t key[4];  // order-preserving keys of the sorted candidates (-0.0 keyed as +0.0)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) key[i] = order_key32(v[i] + 0.0);
       // Each round: the largest head by the top 32 bits of its order-preserving
       // key (one DPP max); when a single lane holds that key its head is the
-      // exact winner, else the tied lanes' heads are compared exactly.
-      for (int r = 0; r < k; ++r) {
-        const uint32_t key = order_key32(v[0] + 0.0);  // -0.0 compares equal to +0.0
-        const uint32_t top_key = wave_max_u32(key);
-        const uint64_t tied = __ballot(key == top_key);
-        double bv;
-        int bi;
-        if (__popcll(tied) == 1) {
-          const int L = (int)__builtin_ctzll(tied);
-          bv = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v[0]), L),
-                                __builtin_amdgcn_readlane(__double2loint(v[0]), L));
-          bi = __builtin_amdgcn_readlane(id[0], L);
-        } else {
-          bv = key == top_key ? v[0] : -__builtin_inf();
-          bi = key == top_key ? id[0] : 0x7FFFFFFF;
-          wave_argmax(bv, bi);
+      // exact winner, else the tied lanes' heads are compared exactly.  The
+      // rounds are unrolled and, apart from that rare tie path, branch-free:
+      // the winning lane shifts its sorted list by one (a popped slot gets key
+      // 0, below every candidate's).
+#pragma unroll
+      for (int r = 0; r < kMaxTopK; ++r) {
+        if (r >= k) break;
+        const uint32_t top_key = wave_max_u32(key[0]);
+        const uint64_t tied = __ballot(key[0] == top_key);
+        int L = (int)__builtin_ctzll(tied);
+        if (__builtin_expect(__popcll(tied) != 1, 0)) {
+          double ev = key[0] == top_key ? v[0] : -__builtin_inf();
+          int ei = key[0] == top_key ? id[0] : 0x7FFFFFFF;
+          wave_argmax(ev, ei);
+          L = (int)__builtin_ctzll(__ballot(key[0] == top_key && id[0] == ei));
         }
-        if (lane == r) {
-          my_v = bv;
-          my_i = bi;
-        }
+        const double bv = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v[0]), L),
+                                           __builtin_amdgcn_readlane(__double2loint(v[0]), L));
+        const int bi = __builtin_amdgcn_readlane(id[0], L);
+        my_v = lane == r ? bv : my_v;
+        my_i = lane == r ? bi : my_i;
         if (B == 1 && lane == 0) {  // for the prefetching waves
           lds_put(&s_pre[r], min(max(bi, 0), E - 1));
           lds_put(&s_pre_n, r + 1);
         }
-        if (id[0] == bi) {  // this lane held the winner: pop it
-          v[0] = v[1];
-          id[0] = id[1];
-          v[1] = v[2];
-          id[1] = id[2];
-          v[2] = v[3];
-          id[2] = id[3];
-          v[3] = -__builtin_inf();
-          id[3] = 0x7FFFFFFF;
+        const bool pop = lane == L;  // this lane held the winner
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          key[i] = pop ? key[i + 1] : key[i];
+          v[i] = pop ? v[i + 1] : v[i];
+          id[i] = pop ? id[i + 1] : id[i];
         }
+        key[3] = pop ? 0u : key[3];
+        v[3] = pop ? -__builtin_inf() : v[3];
+        id[3] = pop ? 0x7FFFFFFF : id[3];
       }
     }
     // Softmax over the k selected logits, summed in rank order, shifted by
@@ -684,9 +687,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
     const double ex = lane < k ? exp(my_v - top) : 0.0;
     double sum = 0.0;
-    for (int r = 0; r < k; ++r)
-      sum += __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(ex), r),
-                              __builtin_amdgcn_readlane(__double2loint(ex), r));
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r)
+      if (r < k)
+        sum += __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(ex), r),
+                                __builtin_amdgcn_readlane(__double2loint(ex), r));
     if (lane < k) {
       my_i = min(max(my_i, 0), E - 1);  // NaN logits can leave no valid candidate: stay in bounds
       s_idx[t * k + lane] = my_i;
