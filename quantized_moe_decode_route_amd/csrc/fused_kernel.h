@@ -852,6 +852,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // partials.
   constexpr int kHB = FD::kUnitW + 4;
   float* sh = reinterpret_cast<float*>(s_buf);  // [S][UPS][kHB]
+  // Vector down in digit-plane form (FD::kDigitH): per (slot, unit) a record
+  // of 24 plane dwords and the unit's exponent k, padded to 28 dwords.
+  constexpr int kHBD = 28;
+  uint32_t* shd = reinterpret_cast<uint32_t*>(s_buf);  // [S][UPS][kHBD]
   const int RPWd = (D + GX - 1) / GX;            // output rows per workgroup
   const int RPV = (RPWd + kW - 1) / kW;          // rows per wave
   const int n0 = jx * RPWd;
@@ -867,7 +871,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   uint8_t* hb = s_buf;
   uint8_t* hsc = hb + (size_t)(S + 1) * kHbSlot;
   float* syp = DNK > 0 ? reinterpret_cast<float*>(hsc + (((size_t)(S + 1) * 4 * DNK + 15) & ~(size_t)15))
-                       : sh + (size_t)S * UPS * kHB;  // [S][rows of this workgroup]
+               : FD::kDigitH ? reinterpret_cast<float*>(shd + (size_t)S * UPS * kHBD)
+                             : sh + (size_t)S * UPS * kHB;  // [S][rows of this workgroup]
   const int UD = RPV * UPS;                      // (row, slice-unit) pairs per wave per expert
   const int ub = lane % UPS;                     // this lane's unit inside the slice row
   // Where this lane's down unit lives: unit xcd*UPS + ub of row n, or, in
@@ -1064,6 +1069,32 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
               if (rr < RPV && rloc < RPWd && n0 + rloc < D) syp[sl * RPWd + rloc] = acc[0][r];
             }
           }
+        }
+      }
+    } else if constexpr (FD::kDigitH) {
+      for (uint32_t m = mask & 0xFFu; m != 0u; m &= m - 1u) {  // tokens ascending
+        const int t = __builtin_ctz(m);
+        const int s = t * k + (int)((mask >> (8 + 3 * t)) & 7u);
+        // The lane's rows share one unit of h: its planes and exponent, read once.
+        const uint4* rec = reinterpret_cast<const uint4*>(shd + (s * UPS + ub) * kHBD);
+        uint32_t pl[24];
+#pragma unroll
+        for (int c = 0; c < 6; ++c) {
+          const uint4 v4 = rec[c];
+          pl[4 * c] = v4.x;
+          pl[4 * c + 1] = v4.y;
+          pl[4 * c + 2] = v4.z;
+          pl[4 * c + 3] = v4.w;
+        }
+        const int ke = (int)rec[6].x;
+#pragma unroll
+        for (int j = 0; j < MAXU_DN; ++j) {
+          const int v = lane + kWave * j;
+          const int rloc = w * RPV + v / UPS;
+          const bool ok = v < UD && rloc < RPWd && n0 + rloc < D;
+          float pr = ok ? FD::dn_dot_digits(src[j], pl, ke) : 0.0f;
+          pr = group_sum_dpp<UPS>(pr);
+          if (ok && ub == 0) syp[s * RPWd + rloc] = pr;
         }
       }
     } else {
@@ -1274,7 +1305,87 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     nr_sink = *reinterpret_cast<const uint32_t*>(a.next_router + (int64_t)g * D + 32 * threadIdx.x);
 
   // ---------------------------------------------------------------- 3. down (partials over the slice)
-  if constexpr (DNK == 0) {
+  if constexpr (DNK == 0 && FD::kDigitH) {
+    __syncthreads();  // the activation view of s_buf is no longer used
+    stamp(traced, s_trace, 11);
+    // Gather this XCD's h slice for every slot in digit-plane form: eight
+    // lanes per (slot, unit) record, four consecutive values each.  The
+    // unit's exponent k puts its largest |h| in [2^21, 2^22) (k = 148 - the
+    // biased exponent of that maximum), N = rint(h * 2^k), and the digits of
+    // N + 0x888888 (base 16, each 0..15) less 8 are the balanced digits
+    // d in [-8, 7], which XOR 8 turns into two's complement nibbles.  A lane
+    // packs its four values' nibbles per plane into a half-word; lane pairs
+    // exchange halves (one DPP swap) so the even lane writes planes 0..2 and
+    // the odd lane planes 3..5 of their code word.
+    static_assert(FD::kUnitW == 32, "eight lanes of four values per unit");
+    constexpr int kR = 3;  // records per lane per pass: all their reads go out before one wait
+    const int NU = S * UPS;
+    const int q8 = lane & 7;
+    const bool odd = (q8 & 1) != 0;
+    const uint64_t t0 = wall_clock64();
+    for (int r0 = 0; r0 < NU; r0 += kR * kW * 8) {
+      auto rid = [&](int r) { return r0 + (r * kW + w) * 8 + (lane >> 3); };
+      auto hp = [&](int q) {
+        const int id = min(rid(q >> 2), NU - 1);
+        const int sl = id / UPS;
+        return ht + (int64_t)sl * Fd + f0 + (id - sl * UPS) * 32 + 4 * q8 + (q & 3);
+      };
+      uint64_t v[4 * kR];
+      bool valid[4 * kR];
+#pragma unroll
+      for (int q = 0; q < 4 * kR; ++q) {
+        valid[q] = rid(q >> 2) < NU;
+        v[q] = valid[q] ? ld_xcd(hp(q)) : 0ull;
+      }
+      const int rr = await_tags<4 * kR>(hp, v, valid, tag, t0, &s_timeout);
+      trace_rereads += rr << 16;
+#pragma unroll
+      for (int r = 0; r < kR; ++r) {
+        if (r0 + (r * kW + w) * 8 >= NU) break;  // the wave's remaining records do not exist
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = valid[4 * r + i] ? __uint_as_float(payload_of(v[4 * r + i])) : 0.0f;
+        float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+        mx = fmaxf(mx, dpp_f<0xB1>(mx));   // quad_perm [1,0,3,2]
+        mx = fmaxf(mx, dpp_f<0x4E>(mx));   // quad_perm [2,3,0,1]
+        mx = fmaxf(mx, dpp_f<0x141>(mx));  // row_half_mirror: the other quad of the eight lanes
+        const int eb = (int)((__float_as_uint(mx) >> 23) & 0xFFu);
+        const int kk = 148 - eb;
+        uint32_t m[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x[i], kk));  // |n| <= 2^22
+          m[i] = (uint32_t)(n + 0x888888) ^ 0x888888u;
+        }
+        uint32_t hw[6];  // plane p: nibble 5 - p of the four values
+#pragma unroll
+        for (int pl = 0; pl < 6; ++pl) {
+          const int sft = 20 - 4 * pl;
+          hw[pl] = ((m[0] >> sft) & 15u) | (((m[1] >> sft) & 15u) << 4) | (((m[2] >> sft) & 15u) << 8) |
+                   (((m[3] >> sft) & 15u) << 12);
+        }
+        const uint32_t send0 = odd ? (hw[0] | (hw[1] << 16)) : (hw[3] | (hw[4] << 16));
+        const uint32_t send1 = odd ? hw[2] : hw[5];
+        const uint32_t recv0 = (uint32_t)dpp_i<0xB1>((int)send0, 0);
+        const uint32_t recv1 = (uint32_t)dpp_i<0xB1>((int)send1, 0);
+        const uint32_t o0 = odd ? ((recv0 & 0xFFFFu) | (hw[3] << 16)) : (hw[0] | (recv0 << 16));
+        const uint32_t o1 = odd ? ((recv0 >> 16) | (hw[4] << 16)) : (hw[1] | (recv0 & 0xFFFF0000u));
+        const uint32_t o2 = odd ? (recv1 | (hw[5] << 16)) : (hw[2] | (recv1 << 16));
+        const int id = rid(r);
+        if (id < NU) {
+          uint32_t* rec = shd + id * kHBD;
+          const int pb = odd ? 3 : 0, wd = q8 >> 1;
+          rec[4 * pb + wd] = o0;
+          rec[4 * (pb + 1) + wd] = o1;
+          rec[4 * (pb + 2) + wd] = o2;
+          if (q8 == 0) rec[24] = eb == 255 ? (uint32_t)kDigitPoison : (uint32_t)kk;
+        }
+      }
+    }
+    stamp(traced, s_trace, 12);
+    if (traced && threadIdx.x == 0) s_trace[13] = (uint64_t)trace_rereads;
+    __syncthreads();
+  } else if constexpr (DNK == 0) {
   __syncthreads();  // the activation view of s_buf is no longer used
   stamp(traced, s_trace, 11);
   {

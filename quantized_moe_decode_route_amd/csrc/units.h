@@ -40,6 +40,9 @@ __device__ __forceinline__ void load_u4(const uint16_t* p, uint32_t* d) {
   d[3] = v.w;
 }
 
+// Marks a unit of h that holds a non-finite value (digit-plane form).
+constexpr int kDigitPoison = 0x7FFFFFFF;
+
 struct MxFmt {
   static constexpr int kUnitW = 32;
   static constexpr int kXDw = 16;  // staged dwords: dword j = x[2j+1] | x[2j] << 16
@@ -106,6 +109,7 @@ struct MxFmt {
     return e8m0_to_f32(e) * acc;
   }
   static constexpr bool kPrepH = false;
+  static constexpr bool kDigitH = false;
   static __device__ __forceinline__ void prep_h(float*) {}
   static __device__ __forceinline__ float dn_dot(const Raw& raw, uint32_t sh, const float* __restrict__ h) {
     return dot(raw, sh, h);
@@ -229,6 +233,7 @@ struct Q2kFmt {
   }
   // Sub-block sums of one unit's h (64 values) into h[64..67].
   static constexpr bool kPrepH = true;
+  static constexpr bool kDigitH = false;
   static __device__ __forceinline__ void prep_h(float* h) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -378,7 +383,28 @@ struct Int4Fmt {
     }
     return bf16_to_f32(raw.s) * __builtin_fmaf(acc, 512.0f, -8.0f * __uint_as_float(xs[16]));
   }
-  // Sum of one unit's h (32 values) into h[32].
+  // Down projection on integer dot products.  The unit's 32 h values are
+  // given as integers N_f = rint(h_f * 2^k) (|N| <= 2^22, one k per unit) in
+  // six planes of balanced base-16 digits (plane p holds digit 5 - p of each
+  // N, two's complement nibbles packed like the codes: element 8w + i in
+  // bits 4i..4i+3 of dword 4p + w).  v_dot8_i32_i4 multiplies eight codes by
+  // eight digits at once; Horner over the planes gives the exact
+  // T = sum_f c_f * N_f (|T| <= 32 * 8 * 2^22 = 2^30), and the unit's
+  // contribution is s * T * 2^-k.  k == kDigitPoison marks a unit with a
+  // non-finite h value (the contribution is NaN).
+  static constexpr bool kDigitH = true;
+  static __device__ __forceinline__ float dn_dot_digits(const Raw& raw, const uint32_t (&pl)[24], int k) {
+    int t = 0;
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {
+      t = p ? t * 16 : 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) t = __builtin_amdgcn_sdot8((int)raw.q[w], (int)pl[4 * p + w], t, false);
+    }
+    const float r = __builtin_amdgcn_ldexpf((float)t * bf16_to_f32(raw.s), -k);
+    return k == kDigitPoison ? __builtin_nanf("") : r;
+  }
+  // Sum of one unit's h (32 values) into h[32] (fp32 h; unused with kDigitH).
   static constexpr bool kPrepH = true;
   static __device__ __forceinline__ void prep_h(float* h) {
     float sum = 0.0f;
