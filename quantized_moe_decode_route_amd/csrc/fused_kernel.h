@@ -796,11 +796,18 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   int U = 0;
   int g_exp;
   uint32_t g_mask, gsl_lo = 0u, gsl_hi = 0u;  // slot tables: filled after gate/up
-  if (B == 1) {  // one token: the groups in rank order (the order of the prefetch)
+  if (B == 1) {  // one token: its k distinct experts, placed in ascending order
     U = k;
-    const int r = min(lane, k - 1);
-    g_exp = s_idx[r];
-    g_mask = 1u | ((uint32_t)r << 8);
+    if (lane < k) {
+      const int ex = s_idx[lane];
+      int pos = 0;
+      for (int r = 0; r < k; ++r) pos += s_idx[r] < ex ? 1 : 0;
+      s_grp[w][pos] = LayerGroup{ex, 1u | ((uint32_t)lane << 8)};
+    }
+    __builtin_amdgcn_wave_barrier();
+    const LayerGroup gr = s_grp[w][min(lane, U - 1)];
+    g_exp = gr.expert;
+    g_mask = gr.mask;
   } else {
 #pragma unroll
     for (int q = 0; q < MOE_MAX_EXPERTS / kWave; ++q) {
@@ -903,6 +910,16 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
   constexpr int kDnSlot = DNK > 0 ? DNK : MAXU_DN;
   typename FD::Raw dring[kRingDN][kDnSlot];
+  // Matrix-core path: per token pair a and k-step, the accumulated down
+  // projection of tokens 2a (columns 0..7) and 2a+1 (columns 8..15) over
+  // their groups, experts ascending (the order is the same at every batch
+  // width, so a token's rows do not depend on the other tokens).
+  typedef float v4f_t __attribute__((ext_vector_type(4)));
+  v4f_t tacc[kMaxTok / 2][DNK > 0 ? DNK : 1];
+#pragma unroll
+  for (int a2 = 0; a2 < kMaxTok / 2; ++a2)
+#pragma unroll
+    for (int ks = 0; ks < (DNK > 0 ? DNK : 1); ++ks) tacc[a2][ks] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
   // Slots past the last expert load this XCD's first h words instead: the
   // h gather has just read them, so the final waits of the ring are cache
   // hits rather than trips to another XCD's weights.
@@ -965,9 +982,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
     for (int b = 0; b < kGatherBatch; ++b) {
       if (i0 + b >= S) break;
+      // The slot's gate weight is folded into h here (fp32 product), so the
+      // matrix cores add a token's experts into one accumulator.
+      const float gws = s_gw[sl[b]];
       float x[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = valid[4 * b + i] ? __uint_as_float(payload_of(v[4 * b + i])) : 0.0f;
+      for (int i = 0; i < 4; ++i) x[i] = valid[4 * b + i] ? gws * __uint_as_float(payload_of(v[4 * b + i])) : 0.0f;
       // The 8 lanes of a 32-value block agree on its exponent e, which puts
       // the block maximum in [128, 256) once scaled by 2^(127 - e).  The
       // terms are base-16 digits of that scaled value: term i is the multiple
@@ -1032,16 +1052,18 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
                     (int)(dok[ks] ? q[3] : 0u), 0, 0, 0, 0};
         ea[ks] = dok[ks] ? (int)e : 127;
       }
-      const int T = __builtin_popcount(mask & 0xFFu);
-      const uint32_t slo = (uint32_t)__builtin_amdgcn_readlane((int)gsl_lo, uu);
-      const uint32_t shi = (uint32_t)__builtin_amdgcn_readlane((int)gsl_hi, uu);
+      // Lane (half hh, column c) takes term c of token 2a + hh when that
+      // token picked the group; other lanes read the zero slot S.
       const int c = mi % kHCols;  // the column's term (none past kHTerms)
-      for (int p0 = 0; p0 < T; p0 += 16 / kHCols) {  // two tokens (x eight columns) per pass
-        const int tt = p0 + mi / kHCols;
-        const bool tok = tt < T;
-        const int sl = tok && c < kHTerms ? (int)(((tt < 4 ? slo : shi) >> (8 * (tt & 3))) & 0xFFu) : S;
-        const int ct = c < kHTerms ? c : 0;
-        v4f acc[DNK];
+      const int hh = mi / kHCols;
+      const int ct = c < kHTerms ? c : 0;
+#pragma unroll
+      for (int a2 = 0; a2 < kMaxTok / 2; ++a2) {
+        if (2 * a2 >= B) break;
+        if (((mask >> (2 * a2)) & 3u) == 0u) continue;  // no token of this pair
+        const int t = 2 * a2 + hh;
+        const bool tok = ((mask >> t) & 1u) != 0u && c < kHTerms;
+        const int sl = tok ? t * k + (int)((mask >> (8 + 3 * t)) & 7u) : S;
 #pragma unroll
         for (int ks = 0; ks < DNK; ++ks) {
           const uint4* bp =
@@ -1049,26 +1071,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
           const uint4 b0 = bp[0], b1 = bp[1];
           const int eb = max((int)hsc[sl * 4 * DNK + 4 * ks + mg] - kHTermStep * ct, 0);
           const v8i Bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-          acc[ks] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[ks], Bv, v4f{0.0f, 0.0f, 0.0f, 0.0f}, 4, 0, 0,
-                                                                     ea[ks], 0, eb);
-        }
-#pragma unroll
-        for (int ks = 1; ks < DNK; ++ks) acc[0] += acc[ks];  // k-steps in order
-        // lane (tt, column c) holds rows 4mg..4mg+3 of column kHCols*tt + c:
-        // sum the token's terms
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[0][r] = group_sum_dpp<kHCols>(acc[0][r]);
-        if (tok && c == 0) {
-          if (dn_full) {  // the wave's 16 rows are all in range: one 16-byte store
-            *reinterpret_cast<float4*>(syp + sl * RPWd + w * 16 + 4 * mg) =
-                make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int rr = 4 * mg + r, rloc = w * RPV + rr;
-              if (rr < RPV && rloc < RPWd && n0 + rloc < D) syp[sl * RPWd + rloc] = acc[0][r];
-            }
-          }
+          tacc[a2][ks] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[ks], Bv, tacc[a2][ks], 4, 0, 0, ea[ks], 0, eb);
         }
       }
     } else if constexpr (FD::kDigitH) {
@@ -1136,11 +1139,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       constexpr int j0 = decltype(j0c)::value;
       typedef int v8i __attribute__((ext_vector_type(8)));
       typedef float v4f __attribute__((ext_vector_type(4)));
-      const int c = mi % kHCols, tt = mi / kHCols;
+      const int c = mi % kHCols, hh = mi / kHCols;  // B <= 2: token hh in half hh (pair 0)
       const int ct = c < kHTerms ? c : 0;
       v8i A[kDnBatch][DNK], Bv[kDnBatch][DNK];
       int ea[kDnBatch][DNK], eb[kDnBatch][DNK], sl[kDnBatch];
-      bool st[kDnBatch];
 #pragma unroll
       for (int b = 0; b < kDnBatch; ++b) {
         const int j = j0 + b;
@@ -1148,11 +1150,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         consume(dring[j]);
         const bool live = j < U;
         const uint32_t mask = grp_mask(live ? j : U - 1);
-        const int T = live ? __builtin_popcount(mask & 0xFFu) : 0;
-        const bool tok = tt < T;
-        const uint32_t tab = (uint32_t)__builtin_amdgcn_readlane((int)gsl_lo, live ? j : U - 1);
-        sl[b] = tok && c < kHTerms ? (int)((tab >> (8 * (tt & 3))) & 0xFFu) : S;
-        st[b] = tok && c == 0;
+        const bool tok = live && hh < B && ((mask >> hh) & 1u) != 0u && c < kHTerms;
+        sl[b] = tok ? hh * k + (int)((mask >> (8 + 3 * hh)) & 7u) : S;
 #pragma unroll
         for (int ks = 0; ks < DNK; ++ks) {
           uint32_t e, q[4];
@@ -1169,19 +1168,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
       for (int b = 0; b < kDnBatch; ++b) {
         const int j = j0 + b;
-        if (j >= kRingDN - 1) continue;
-        v4f acc[DNK];
+        if (j >= kRingDN - 1 || j >= U) continue;  // past the last group: its slot holds no weights
 #pragma unroll
         for (int ks = 0; ks < DNK; ++ks)
-          acc[ks] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[b][ks], Bv[b][ks], v4f{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                     4, 0, 0, ea[b][ks], 0, eb[b][ks]);
-#pragma unroll
-        for (int ks = 1; ks < DNK; ++ks) acc[0] += acc[ks];  // k-steps in order
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[0][r] = group_sum_dpp<kHCols>(acc[0][r]);
-        if (st[b])
-          *reinterpret_cast<float4*>(syp + sl[b] * RPWd + w * 16 + 4 * mg) =
-              make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+          tacc[0][ks] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[b][ks], Bv[b][ks], tacc[0][ks], 4, 0, 0,
+                                                                         ea[b][ks], 0, eb[b][ks]);
       }
     }
   };
@@ -1467,12 +1458,40 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       }
     }
   }
+  if constexpr (DNK > 0) {
+    // Each wave publishes its rows of this XCD's partial output for every
+    // token straight from its accumulators (the gate weights are already in
+    // h): k-steps in order, then the token's terms (an 8-lane DPP sum).  No
+    // workgroup barrier: nothing in LDS is read after this point.
+    stamp(traced, s_trace, 8);
+    uint64_t* pt = reinterpret_cast<uint64_t*>(a.ws + a.L.part_tags);  // [NX][B][D]
+    const int c = mi % kHCols, hh = mi / kHCols;
+#pragma unroll
+    for (int a2 = 0; a2 < kMaxTok / 2; ++a2) {
+      if (2 * a2 >= B) break;
+      v4f_t v = tacc[a2][0];
+#pragma unroll
+      for (int ks = 1; ks < DNK; ++ks) v += tacc[a2][ks];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = group_sum_dpp<kHCols>(v[r]);
+      const int t = 2 * a2 + hh;
+      if (c == 0 && t < B) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = 4 * mg + r, rloc = w * RPV + rr;
+          if (rr < RPV && rloc < RPWd && n0 + rloc < D)
+            st_dev(pt + ((int64_t)xcd * B + t) * D + n0 + rloc, tagged(__float_as_uint(v[r]), tag));
+        }
+      }
+    }
+  } else {
   __syncthreads();
   stamp(traced, s_trace, 8);
-  // Combine the k ranks in rank order and publish this XCD's partial rows
-  // (first half of the waves), while the second half gathers the partials of
-  // the rows this workgroup finishes.
-  if (w < kW / 2) {
+  }
+  // Vector path: combine the k ranks in rank order and publish this XCD's
+  // partial rows (first half of the waves), while the second half gathers the
+  // partials of the rows this workgroup finishes.
+  if (DNK == 0 && w < kW / 2) {
     uint64_t* pt = reinterpret_cast<uint64_t*>(a.ws + a.L.part_tags);  // [NX][B][D]
     for (int i = threadIdx.x; i < B * RPWd; i += (kW / 2) * kWave) {
       const int t = i / RPWd, rl = i - (i / RPWd) * RPWd;
