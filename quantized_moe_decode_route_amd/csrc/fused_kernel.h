@@ -869,8 +869,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // Matrix-core down projection (MXFP4 in MOE_LAYOUT_MFMA16, DNK > 0): the
   // h slice of every slot becomes the B operand of the 16x16x128 scaled
   // MFMA as kHTerms fp8 (E4M3) terms per value, each term with its own E8M0
-  // exponent: h = sum_i c_i * 2^(e - 4i - 127), c_i a multiple of 16 in
-  // [-256, 256], one e per 32 values (see gather_batch).  hb: [S][DNK][4 lane groups][kHTerms terms][32 bytes];
+  // exponent: h ~ sum_i d_i * 2^(e - 4i - 127), d_i an integer in [-8, 7],
+  // one e per 32 values (see gather_batch; the slot's gate weight is folded
+  // in).  hb: [S][DNK][4 lane groups][kHTerms terms][32 bytes];
   // hsc: [S][4 * DNK] exponents e.  Both take the LDS of the activations,
   // which are dead once gate/up has ended.  Slot S of hb/hsc is all zeros:
   // lanes without a token (or term) read it.
@@ -988,49 +989,46 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       float x[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) x[i] = valid[4 * b + i] ? gws * __uint_as_float(payload_of(v[4 * b + i])) : 0.0f;
-      // The 8 lanes of a 32-value block agree on its exponent e, which puts
-      // the block maximum in [128, 256) once scaled by 2^(127 - e).  The
-      // terms are base-16 digits of that scaled value: term i is the multiple
-      // of 16 nearest to what the earlier terms left, scaled by 2^(4i) (E8M0
-      // exponent e_i = e - 4i), so every term lies in {0, +-16, ..., +-256},
-      // is exact in E4M3, and the B values of one column span only the
-      // binades 2^4 .. 2^8.  (The scaled MFMA sums products whose exponents
-      // lie in such a narrow band exactly; a B column holding values from all
-      // of E4M3's range loses the smallest products.)  A remainder is at most
-      // 8, 128 once scaled by 2^4; six terms leave |error| <= 2^-24 * the
-      // block maximum (fp32 resolution).
+      // The 8 lanes of a 32-value block agree on its exponent k, which puts
+      // the block maximum times 2^k in [2^21, 2^22) (k = 148 - the biased
+      // exponent of the maximum, at most 127).  N = rint(h * 2^k) is written
+      // in six balanced base-16 digits d_i in [-8, 7] (the digits of
+      // N + 0x888888 less 8, two's complement nibbles after XOR 8): term i is
+      // d_i, exact in E4M3, under the E8M0 exponent 147 - k - 4i stored as
+      // 147 - k (255 for a block holding a non-finite value, which makes
+      // every term's scale NaN).  The B values of one column thus span only
+      // the binades 2^0 .. 2^3: the scaled MFMA sums products whose exponents
+      // lie in such a narrow band exactly, while a B column holding values
+      // from all of E4M3's range loses the smallest products.
+      // |error| <= 2^-22 * the block maximum.
       float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
       mx = fmaxf(mx, dpp_f<0xB1>(mx));   // quad_perm [1,0,3,2]
       mx = fmaxf(mx, dpp_f<0x4E>(mx));   // quad_perm [2,3,0,1]
       mx = fmaxf(mx, dpp_f<0x141>(mx));  // row_half_mirror: the other quad of the 8
-      const int e = max((int)((__float_as_uint(mx) >> 23) & 0xFFu) - 7, 1);
-      const float scale = __uint_as_float((uint32_t)(254 - e) << 23);  // 2^(127 - e), exact
+      const int ebm = (int)((__float_as_uint(mx) >> 23) & 0xFFu);
+      const int kk = min(148 - ebm, 127);
+      uint32_t m[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] *= scale;
+      for (int i = 0; i < 4; ++i) {
+        const int n = (int)__builtin_rintf(__builtin_amdgcn_ldexpf(x[i], kk));  // |n| <= 2^22
+        m[i] = (uint32_t)(n + 0x888888) ^ 0x888888u;
+      }
       // hb byte q of lane group g, k-step ks, term i holds value 128ks +
       // 64(q/16) + 16g + ((q%16)^1): the E2M1 nibble order pairs weight 2j+1
       // with the lower K position, so values are stored pair-swapped.
       const int r = fl & 127, ks = fl >> 7;
       uint32_t* dst = reinterpret_cast<uint32_t*>(
           hb + (size_t)sl[b] * kHbSlot + ((ks * 4 + ((r & 63) >> 4)) * kHTerms) * 32 + (r >> 6) * 16 + (r & 15));
-      int et = e;
 #pragma unroll
       for (int term = 0; term < kHTerms; ++term) {
-        float t[4];
+        float t[4];  // digit 5 - term of each N (bits 20 - 4 term .. 23 - 4 term), sign-extended
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] = 16.0f * __builtin_rintf(x[i] * 0.0625f);  // exact multiple of 16
+        for (int i = 0; i < 4; ++i) t[i] = (float)(((int)(m[i] << (8 + 4 * term))) >> 28);
         int d = __builtin_amdgcn_cvt_pk_fp8_f32(t[1], t[0], 0, false);
         d = __builtin_amdgcn_cvt_pk_fp8_f32(t[3], t[2], d, true);
         if (act) dst[term * 8] = (uint32_t)d;
-        if (term + 1 < kHTerms) {
-          const int en = max(et - kHTermStep, 0);
-          const float up = __uint_as_float((uint32_t)(127 + et - en) << 23);  // 2^(e_i - e_(i+1)), exact
-          et = en;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) x[i] = (x[i] - t[i]) * up;  // exact
-        }
       }
-      if (act && (lane & 7) == 0) hsc[sl[b] * 4 * DNK + (fl >> 5)] = (uint8_t)e;
+      if (act && (lane & 7) == 0) hsc[sl[b] * 4 * DNK + (fl >> 5)] = (uint8_t)(ebm == 255 ? 255 : 147 - kk);
     }
     return true;
   };
@@ -1069,7 +1067,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
           const uint4* bp =
               reinterpret_cast<const uint4*>(hb + (size_t)sl * kHbSlot + ((ks * 4 + mg) * kHTerms + ct) * 32);
           const uint4 b0 = bp[0], b1 = bp[1];
-          const int eb = max((int)hsc[sl * 4 * DNK + 4 * ks + mg] - kHTermStep * ct, 0);
+          const int hs = hsc[sl * 4 * DNK + 4 * ks + mg];
+          const int eb = hs == 255 ? 255 : max(hs - kHTermStep * ct, 0);
           const v8i Bv = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
           tacc[a2][ks] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[ks], Bv, tacc[a2][ks], 4, 0, 0, ea[ks], 0, eb);
         }
@@ -1162,7 +1161,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
               reinterpret_cast<const uint4*>(hb + (size_t)sl[b] * kHbSlot + ((ks * 4 + mg) * kHTerms + ct) * 32);
           const uint4 b0 = bp[0], b1 = bp[1];
           Bv[b][ks] = v8i{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
-          eb[b][ks] = max((int)hsc[sl[b] * 4 * DNK + 4 * ks + mg] - kHTermStep * ct, 0);
+          const int hs = hsc[sl[b] * 4 * DNK + 4 * ks + mg];
+          eb[b][ks] = hs == 255 ? 255 : max(hs - kHTermStep * ct, 0);
         }
       }
 #pragma unroll
