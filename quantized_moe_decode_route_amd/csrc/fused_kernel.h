@@ -685,17 +685,18 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
         top = fmax(top, __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_v), r),
                                          __builtin_amdgcn_readlane(__double2loint(my_v), r)));
     }
-    const double ex = lane < k ? exp(my_v - top) : 0.0;
-    double sum = 0.0;
+    // The gate weights are fp32 outputs: the exponentials, their rank-order
+    // sum and the quotients are taken in fp32 (the fp64 difference rounded
+    // once), which keeps them within a few fp32 units of the exact weights.
+    const float ex = lane < k ? expf((float)(my_v - top)) : 0.0f;
+    float sum = 0.0f;
 #pragma unroll
     for (int r = 0; r < kMaxTopK; ++r)
-      if (r < k)
-        sum += __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(ex), r),
-                                __builtin_amdgcn_readlane(__double2loint(ex), r));
+      if (r < k) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), r));
     if (lane < k) {
       my_i = min(max(my_i, 0), E - 1);  // NaN logits can leave no valid candidate: stay in bounds
       s_idx[t * k + lane] = my_i;
-      s_gw[t * k + lane] = (float)(ex / sum);
+      s_gw[t * k + lane] = ex / sum;
       // bit t: token t picked the expert; bits 8+3t..10+3t: at rank `lane`
       atomicOr(&s_mask[my_i], (1u << t) | ((uint32_t)lane << (8 + 3 * t)));
     }
