@@ -345,11 +345,13 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     for (int t = 0; t < kMaxTok; ++t) fx[t] = *reinterpret_cast<const uint4*>(x_in + (int64_t)min(t, B - 1) * D + c8);
   }
   uint32_t* ctr = reinterpret_cast<uint32_t*>(ws + ctr_off);
-  // This call's epoch, read with a scalar load: a vector load here would
-  // make the first use of the tag wait for the x and atomic requests issued
-  // after it.  Its first use is deferred to the first publication (the asm
-  // in tag_now), so the scalar waits before it do not include this load.
-  // (Workgroup 0 advances the counter only after every workgroup has read it.)
+  // This call's epoch, read with a scalar load issued after the router and
+  // activation loads: a vector load of it measured slower (agent-coherent
+  // reads of the counter), and a plain one would make the first use of the
+  // tag wait for the x and atomic requests issued after it.  Its value is
+  // used from the first publication on (tag_now); the compiler may still
+  // wait for it earlier, together with later argument loads.  (Workgroup 0
+  // advances the counter only after every workgroup has read it.)
   typedef const __attribute__((address_space(4))) uint32_t ConstU32;
   uint32_t epoch = ((ConstU32*)ctr)[kCtrEpoch];
   uint32_t tag = 0u;
