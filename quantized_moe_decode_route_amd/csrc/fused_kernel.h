@@ -1570,6 +1570,17 @@ hipError_t launch_fused_f(const FusedArgs& a, int grid, int gu_units, int dn_uni
                             : launch_fused_t<F, 1, 1, UPS, DNK, NORM, FD>(a, grid, s);
   } else {
     static_assert(!NORM, "the in-kernel norm is built for the matrix-core path");
+    // one-token builds of the full layer shape (d_model 4096, one 256-column
+    // d_ff slice per XCD: eight 32-wide or four 64-wide down units)
+    if constexpr (UPS == 8) {
+      if (a.B == 1 && gu_units > kWave && dn_units > kWave)
+        return launch_fused_t<F, 2, 2, UPS, 0, false, FD, true>(a, grid, s);
+    }
+    if constexpr (UPS == 4) {
+      if (a.B == 1 && dn_units <= kWave)
+        return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, 0, false, FD, true>(a, grid, s)
+                                : launch_fused_t<F, 1, 1, UPS, 0, false, FD, true>(a, grid, s);
+    }
     if (gu_units > kWave) {
       return dn_units > kWave ? launch_fused_t<F, 2, 2, UPS, 0, false, FD>(a, grid, s)
                               : launch_fused_t<F, 2, 1, UPS, 0, false, FD>(a, grid, s);
