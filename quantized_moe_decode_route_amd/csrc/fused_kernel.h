@@ -295,11 +295,12 @@ static_assert(kHTerms <= kHCols && 16 % kHCols == 0, "a token's terms fit its co
 constexpr int kPrefetchExperts = 1;  // one token: experts whose gate/up rows go to L2 during top-k
 constexpr bool kPrefetchDown = true;  // ... and their down rows
 
-// F: format of gate and up; FD: format of down.  ONE: built for one token
-// (B = 1 known at compile time; the in-kernel norm implies it).
-template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD, bool ONE = NORM>
+// F: format of gate and up; FD: format of down.  CB: the batch width when it
+// is known at compile time (0: given at run time; the in-kernel norm implies
+// one token).
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD, int CB = NORM ? 1 : 0>
 __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a) {
-  static_assert(!NORM || ONE, "the in-kernel norm is built for one token");
+  static_assert(!NORM || CB == 1, "the in-kernel norm is built for one token");
   constexpr int kCh = F::kXDw / 4;  // 16-byte chunks of one unit's staged activations
   constexpr int kRingGU = Rings<F>::kGU;
   constexpr int kRingDN = Rings<FD>::kDN;
@@ -323,7 +324,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   const float* h_in = as_global<const float>(h_i);
   uint8_t* ws = as_global<uint8_t>(ws_i);
   const bool traced = trace_i != 0u;
-  const int B = ONE ? 1 : Bv, Fd = a.Fd;
+  const int B = CB ? CB : Bv, Fd = a.Fd;
   const int S = B * k;  // (token, rank) slots
   const uint64_t t_start = wall_clock64();  // trace slot 0 (kept in a register until the LDS record is set up)
   // First requests: this thread's 8-element chunk of the workgroup's router
@@ -1548,10 +1549,10 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   asm volatile("" ::"v"(nr_sink));  // the next layer's router line, long since arrived
 }
 
-template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD, bool ONE = NORM>
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD, int CB = NORM ? 1 : 0>
 hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
-  if (ONE && a.B != 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK, NORM, FD, ONE>), dim3(grid),
+  if (CB && a.B != CB) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK, NORM, FD, CB>), dim3(grid),
                      dim3(kW * kWave), 0, s, a);
   return hipGetLastError();
 }
@@ -1562,24 +1563,33 @@ hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
 template <class F, int UPS, int DNK, bool NORM = false, class FD = F>
 hipError_t launch_fused_f(const FusedArgs& a, int grid, int gu_units, int dn_units, hipStream_t s) {
   if constexpr (DNK > 0) {
-    // the full layer shape (d_model > 2048, eight units per XCD slice) has a
-    // one-token build of its own
-    if constexpr (!NORM && UPS == 8)
-      if (gu_units > kWave && a.B == 1) return launch_fused_t<F, 2, 1, UPS, DNK, false, FD, true>(a, grid, s);
+    // the full layer shape (d_model > 2048, eight units per XCD slice) has
+    // builds of its own for one and for eight tokens
+    if constexpr (!NORM && UPS == 8) {
+      if (gu_units > kWave && a.B == 1) return launch_fused_t<F, 2, 1, UPS, DNK, false, FD, 1>(a, grid, s);
+      if (gu_units > kWave && a.B == 8) return launch_fused_t<F, 2, 1, UPS, DNK, false, FD, 8>(a, grid, s);
+    }
     return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, DNK, NORM, FD>(a, grid, s)
                             : launch_fused_t<F, 1, 1, UPS, DNK, NORM, FD>(a, grid, s);
   } else {
     static_assert(!NORM, "the in-kernel norm is built for the matrix-core path");
-    // one-token builds of the full layer shape (d_model 4096, one 256-column
-    // d_ff slice per XCD: eight 32-wide or four 64-wide down units)
+    // one- and eight-token builds of the full layer shape (d_model 4096, one
+    // 256-column d_ff slice per XCD: eight 32-wide or four 64-wide down units)
     if constexpr (UPS == 8) {
-      if (a.B == 1 && gu_units > kWave && dn_units > kWave)
-        return launch_fused_t<F, 2, 2, UPS, 0, false, FD, true>(a, grid, s);
+      if (gu_units > kWave && dn_units > kWave) {
+        if (a.B == 1) return launch_fused_t<F, 2, 2, UPS, 0, false, FD, 1>(a, grid, s);
+        if (a.B == 8) return launch_fused_t<F, 2, 2, UPS, 0, false, FD, 8>(a, grid, s);
+      }
     }
     if constexpr (UPS == 4) {
-      if (a.B == 1 && dn_units <= kWave)
-        return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, 0, false, FD, true>(a, grid, s)
-                                : launch_fused_t<F, 1, 1, UPS, 0, false, FD, true>(a, grid, s);
+      if (dn_units <= kWave) {
+        if (a.B == 1)
+          return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, 0, false, FD, 1>(a, grid, s)
+                                  : launch_fused_t<F, 1, 1, UPS, 0, false, FD, 1>(a, grid, s);
+        if (a.B == 8)
+          return gu_units > kWave ? launch_fused_t<F, 2, 1, UPS, 0, false, FD, 8>(a, grid, s)
+                                  : launch_fused_t<F, 1, 1, UPS, 0, false, FD, 8>(a, grid, s);
+      }
     }
     if (gu_units > kWave) {
       return dn_units > kWave ? launch_fused_t<F, 2, 2, UPS, 0, false, FD>(a, grid, s)
