@@ -295,10 +295,16 @@ static_assert(kHTerms <= kHCols && 16 % kHCols == 0, "a token's terms fit its co
 constexpr int kPrefetchExperts = 1;  // one token: experts whose gate/up rows go to L2 during top-k
 constexpr bool kPrefetchDown = true;  // ... and their down rows
 
+// The layer shape of the benchmark workloads (256 experts, top 6, d_model
+// 4096, d_ff 2048) on a device of 256 compute units in 8 XCDs: builds with
+// FULL = true take these as compile-time constants.
+constexpr int kFullE = 256, kFullK = 6, kFullD = 4096, kFullF = 2048, kFullG = 256, kFullNX = 8;
+
 // F: format of gate and up; FD: format of down.  CB: the batch width when it
 // is known at compile time (0: given at run time; the in-kernel norm implies
-// one token).
-template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD, int CB = NORM ? 1 : 0>
+// one token).  FULL: the shape above, known at compile time.
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD, int CB = NORM ? 1 : 0,
+          bool FULL = false>
 __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a) {
   static_assert(!NORM || CB == 1, "the in-kernel norm is built for one token");
   constexpr int kCh = F::kXDw / 4;  // 16-byte chunks of one unit's staged activations
@@ -318,13 +324,21 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   uint64_t ctr_off = a.L.counters, lg_off = a.L.logit_tags, trace_i = (uint64_t)a.trace;
   int G = gridDim.x, NX = a.nx, E = a.E, D = a.D, Bv = a.B, k = a.k;
   asm volatile("" : "+s"(router_i), "+s"(x_i), "+s"(h_i), "+s"(ws_i), "+s"(ctr_off), "+s"(lg_off), "+s"(trace_i));
-  asm volatile("" : "+s"(G), "+s"(NX), "+s"(E), "+s"(D), "+s"(Bv), "+s"(k));
+  if constexpr (FULL) {
+    G = kFullG;
+    NX = kFullNX;
+    E = kFullE;
+    D = kFullD;
+    k = kFullK;
+  } else {
+    asm volatile("" : "+s"(G), "+s"(NX), "+s"(E), "+s"(D), "+s"(Bv), "+s"(k));
+  }
   const float* router_w = as_global<const float>(router_i);
   const uint16_t* x_in = as_global<const uint16_t>(x_i);
   const float* h_in = as_global<const float>(h_i);
   uint8_t* ws = as_global<uint8_t>(ws_i);
   const bool traced = trace_i != 0u;
-  const int B = CB ? CB : Bv, Fd = a.Fd;
+  const int B = CB ? CB : Bv, Fd = FULL ? kFullF : a.Fd;
   const int S = B * k;  // (token, rank) slots
   const uint64_t t_start = wall_clock64();  // trace slot 0 (kept in a register until the LDS record is set up)
   // First requests: this thread's 8-element chunk of the workgroup's router
@@ -1549,10 +1563,16 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   asm volatile("" ::"v"(nr_sink));  // the next layer's router line, long since arrived
 }
 
-template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD, int CB = NORM ? 1 : 0>
+__host__ __forceinline__ bool full_shape(const FusedArgs& a, int grid) {
+  return a.E == kFullE && a.k == kFullK && a.D == kFullD && a.Fd == kFullF && a.nx == kFullNX && grid == kFullG;
+}
+
+template <class F, int MAXU_GU, int MAXU_DN, int UPS, int DNK, bool NORM, class FD, int CB = NORM ? 1 : 0,
+          bool FULL = false>
 hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
   if (CB && a.B != CB) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK, NORM, FD, CB>), dim3(grid),
+  if (FULL && !full_shape(a, grid)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fused_layer_kernel<F, MAXU_GU, MAXU_DN, UPS, DNK, NORM, FD, CB, FULL>), dim3(grid),
                      dim3(kW * kWave), 0, s, a);
   return hipGetLastError();
 }
@@ -1562,6 +1582,19 @@ hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
 // matrix-core path only.  FD: format of the down projection.
 template <class F, int UPS, int DNK, bool NORM = false, class FD = F>
 hipError_t launch_fused_f(const FusedArgs& a, int grid, int gu_units, int dn_units, hipStream_t s) {
+  // The benchmark shape: builds with every shape parameter known at compile
+  // time, at eight tokens and, on the vector down path, at one token.  (The
+  // one-token matrix-core build measured slower with the shape fixed, so it
+  // and the in-kernel-norm build keep only the batch width.)
+  if constexpr (kFullF / kFullNX / FD::kUnitW == UPS && !NORM) {
+    constexpr int kGu = kFullD / F::kUnitW > kWave ? 2 : 1;
+    constexpr int kDn = DNK > 0 ? 1 : (16 * UPS > kWave ? 2 : 1);  // 16 output rows per wave
+    if (full_shape(a, grid) && gu_units == kFullD / F::kUnitW) {
+      if constexpr (DNK == 0)
+        if (a.B == 1) return launch_fused_t<F, kGu, kDn, UPS, 0, false, FD, 1, true>(a, grid, s);
+      if (a.B == 8) return launch_fused_t<F, kGu, kDn, UPS, DNK, false, FD, 8, true>(a, grid, s);
+    }
+  }
   if constexpr (DNK > 0) {
     // the full layer shape (d_model > 2048, eight units per XCD slice) has
     // builds of its own for one and for eight tokens
