@@ -400,13 +400,22 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   int trace_rereads = 0;  // thread 0: re-read passes of the logit (low half) and h (high half) waits
   if (threadIdx.x == 0) s_timeout = 0;
   if (traced && threadIdx.x < kTracePoints) s_trace[threadIdx.x] = 0ull;  // slots a path does not stamp read 0
-  // Requested right after this thread's first router loads (its result is
-  // needed only after the logits), so nothing waits for it before them.
+  // Requested once the first router dot has consumed its loads (its result
+  // is needed only after the logits).  Thread 0 alone issues it, so the
+  // compiler cannot count it at a wait that follows it: a wait for the router
+  // row issued after it becomes a wait for every request, the contended
+  // atomic's return included.  take_arrival_after orders it behind the
+  // partial sums (an empty asm reading them).
   bool arrival_pending = true;
   auto take_arrival = [&]() {
     if (arrival_pending && threadIdx.x == 0)
       xcd_arrival = __hip_atomic_fetch_add(ctr + kCtrXcdBase + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     arrival_pending = false;
+  };
+  auto take_arrival_after = [&](const double (&acc)[kMaxTok]) {
+#pragma unroll
+    for (int t = 0; t < kMaxTok; ++t) asm volatile("" ::"v"(acc[t]));
+    take_arrival();
   };
   static_assert(MOE_MAX_EXPERTS <= kW * kWave, "one expert word per thread");
   if (threadIdx.x < MOE_MAX_EXPERTS) s_mask[threadIdx.x] = 0u;
@@ -478,7 +487,6 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     // the norm then waits for h alone while the router row is in flight.
     const bool mine = 8 * (int)threadIdx.x < D;  // then c8 = 8 * threadIdx.x
     float4 ha = fha, hb = fhb, w0 = fw0, w1 = fw1;
-    take_arrival();
     if (!mine) ha = hb = make_float4(0.f, 0.f, 0.f, 0.f);
     const double ss = wave_sum_dpp_f64(rms_squares8(ha, hb, 0.0));
     if (lane == kWave - 1) s_rms[w] = ss;
@@ -501,6 +509,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
       for (int t = 0; t < kMaxTok; ++t) acc[t] = 0.0;
       if (mine) dot8(acc, w0, w1, xall);
+      take_arrival_after(acc);
       publish_logits(e, acc);
     }
   } else {
@@ -517,8 +526,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
 #pragma unroll
         for (int t = 0; t < kMaxTok; ++t)
           xall[t] = *reinterpret_cast<const uint4*>(x_in + (int64_t)min(t, B - 1) * D + c);
-        take_arrival();
         dot8(acc, w0, w1, xall);
+        take_arrival_after(acc);
         if (e == g) {
 #pragma unroll
           for (int t = 0; t < kMaxTok; ++t) xkeep[t] = xall[t];
@@ -529,8 +538,8 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       if (D <= 8 * kW * kWave) {
         if (e == g) {  // the chunk requested first
           if (8 * (int)threadIdx.x < D) {
-            take_arrival();
             dot8(acc, fw0, fw1, fx);
+            take_arrival_after(acc);
 #pragma unroll
             for (int t = 0; t < kMaxTok; ++t) xkeep[t] = fx[t];
           }
