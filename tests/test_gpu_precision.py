@@ -40,3 +40,26 @@ def test_error_distribution(shape, layout, B):
     assert max(errs) <= 1e-4
     del L
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("shape", ["full", "small"])
+@pytest.mark.parametrize("fmt", ["int4g32", "q2k"])
+@pytest.mark.parametrize("B", [1, 8])
+def test_error_distribution_vector_formats(shape, fmt, B):
+    """The same distribution for the formats whose down projection runs on the
+    vector path (256-column tiled down): INT4 group-32, whose down dot takes h
+    as six planes of base-16 digits against the stored codes, and Q2_K."""
+    E, D, F = (256, 4096, 2048) if shape == "full" else (16, 512, 256)
+    L = Layer(fmt, 0x5EED + 200, 0, E, D, F, 6, down_layout="tile256")
+    errs = []
+    ws = L.workspace(B)
+    for i in range(32 // B):
+        xb = synth.token_bf16(9500 + i, B, D)
+        y, idx, _ = L.run(xb, ws)
+        yo, io, _ = L.oracle(xb)
+        assert np.array_equal(idx, io)
+        errs.extend(rel_inf_err(y, yo).tolist())
+    print(f"\n{shape} {fmt} tile256 B={B} ({len(errs)} tokens): {_dist(errs)}")
+    assert max(errs) <= 1e-4
+    del L
+    torch.cuda.empty_cache()
