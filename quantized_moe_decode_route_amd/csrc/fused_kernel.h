@@ -1473,9 +1473,17 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     for (int j = 0; j < kRingDN - 1; ++j)
       if (j < U) compute_dn(j, dring[j]);
   } else {
+    // Waves w and w + kW/2 share a SIMD and have the same fixed down work;
+    // the issue arbiter favours the older wave of a pair, which left the
+    // younger waves several microseconds behind at eight tokens (and the
+    // finish waits for the last rows).  The pair swaps priority every group.
     for (int base = 0; base < U; base += kRingDN) {
 #pragma unroll
       for (int j = 0; j < kRingDN; ++j) {
+        if (((j + (w >= kW / 2 ? 1 : 0)) & 1) != 0)
+          __builtin_amdgcn_s_setprio(1);
+        else
+          __builtin_amdgcn_s_setprio(0);
         load_dn(base + j + kRingDN - 1, dring[(j + kRingDN - 1) % kRingDN]);
         __builtin_amdgcn_sched_barrier(0);
         if (base + j < U)
@@ -1484,6 +1492,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
           consume(dring[j]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   if constexpr (DNK > 0) {
     // Each wave publishes its rows of this XCD's partial output for every
