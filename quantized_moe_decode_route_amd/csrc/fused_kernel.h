@@ -324,7 +324,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   uint64_t ctr_off = a.L.counters, lg_off = a.L.logit_tags, trace_i = (uint64_t)a.trace;
   int G = gridDim.x, NX = a.nx, E = a.E, D = a.D, Bv = a.B, k = a.k;
   asm volatile("" : "+s"(router_i), "+s"(x_i), "+s"(h_i), "+s"(ws_i), "+s"(ctr_off), "+s"(lg_off), "+s"(trace_i));
-  if constexpr (FULL) {
+  // Full-shape builds take the shape as constants: the vector-path builds
+  // from the first instruction, the matrix-core builds from gate/up on (their
+  // routing measured 1.3 us slower at one token with the constants in it,
+  // their later phases faster).
+  constexpr bool kConstAll = FULL && DNK == 0, kConstLate = FULL && DNK > 0;
+  if constexpr (kConstAll) {
     G = kFullG;
     NX = kFullNX;
     E = kFullE;
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   uint8_t* ws = as_global<uint8_t>(ws_i);
   const bool traced = trace_i != 0u;
   const int B = CB ? CB : Bv, Fd = FULL ? kFullF : a.Fd;
-  const int S = B * k;  // (token, rank) slots
+  int S = B * k;  // (token, rank) slots
   const uint64_t t_start = wall_clock64();  // trace slot 0 (kept in a register until the LDS record is set up)
   // First requests: this thread's 8-element chunk of the workgroup's router
   // row and of the activations (x, or h for the in-kernel norm), issued
@@ -392,7 +397,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   __shared__ __align__(16) uint8_t s_buf[kLdsBytes];
 
   const int xcd = (int)xcc_id();
-  const int GX = G / NX;  // workgroups per XCD
+  int GX = G / NX;  // workgroups per XCD
   // Index inside the XCD: every call adds exactly GX to each XCD's counter.
   // The result is first used after the router logits, so its latency hides
   // behind them.
@@ -425,7 +430,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     s_pre_n = 0;
   }
 
-  const int UG = F::units(D);
+  int UG = F::units(D);
   uint32_t xraw[2][F::kXRaw];
   // With x given, a workgroup with a router row stages the activations from
   // the chunks it loads for the logits (thread i holds elements 8i..8i+7 of
@@ -872,6 +877,16 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   }
   stamp(traced, s_trace, 5);
 
+  if constexpr (kConstLate) {  // the same values, now as constants
+    G = kFullG;
+    NX = kFullNX;
+    E = kFullE;
+    D = kFullD;
+    k = kFullK;
+    GX = kFullG / kFullNX;
+    S = B * kFullK;
+    UG = F::units(kFullD);
+  }
   // ---------------------------------------------------------------- 2. gate / up
   const int jx = s_jx;     // index inside the XCD
   const int FS = Fd / NX;  // d_ff slice of this XCD
@@ -1601,15 +1616,13 @@ hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
 template <class F, int UPS, int DNK, bool NORM = false, class FD = F>
 hipError_t launch_fused_f(const FusedArgs& a, int grid, int gu_units, int dn_units, hipStream_t s) {
   // The benchmark shape: builds with every shape parameter known at compile
-  // time, at eight tokens and, on the vector down path, at one token.  (The
-  // one-token matrix-core build measured slower with the shape fixed, so it
-  // and the in-kernel-norm build keep only the batch width.)
+  // time, at one and at eight tokens.  (The in-kernel-norm build keeps only
+  // the batch width.)
   if constexpr (kFullF / kFullNX / FD::kUnitW == UPS && !NORM) {
     constexpr int kGu = kFullD / F::kUnitW > kWave ? 2 : 1;
     constexpr int kDn = DNK > 0 ? 1 : (16 * UPS > kWave ? 2 : 1);  // 16 output rows per wave
     if (full_shape(a, grid) && gu_units == kFullD / F::kUnitW) {
-      if constexpr (DNK == 0)
-        if (a.B == 1) return launch_fused_t<F, kGu, kDn, UPS, 0, false, FD, 1, true>(a, grid, s);
+      if (a.B == 1) return launch_fused_t<F, kGu, kDn, UPS, DNK, false, FD, 1, true>(a, grid, s);
       if (a.B == 8) return launch_fused_t<F, kGu, kDn, UPS, DNK, false, FD, 8, true>(a, grid, s);
     }
   }
