@@ -1616,14 +1616,14 @@ hipError_t launch_fused_t(const FusedArgs& a, int grid, hipStream_t s) {
 template <class F, int UPS, int DNK, bool NORM = false, class FD = F>
 hipError_t launch_fused_f(const FusedArgs& a, int grid, int gu_units, int dn_units, hipStream_t s) {
   // The benchmark shape: builds with every shape parameter known at compile
-  // time, at one and at eight tokens.  (The in-kernel-norm build keeps only
-  // the batch width.)
-  if constexpr (kFullF / kFullNX / FD::kUnitW == UPS && !NORM) {
+  // time, at one and at eight tokens (the in-kernel norm: one token).
+  if constexpr (kFullF / kFullNX / FD::kUnitW == UPS) {
     constexpr int kGu = kFullD / F::kUnitW > kWave ? 2 : 1;
     constexpr int kDn = DNK > 0 ? 1 : (16 * UPS > kWave ? 2 : 1);  // 16 output rows per wave
     if (full_shape(a, grid) && gu_units == kFullD / F::kUnitW) {
-      if (a.B == 1) return launch_fused_t<F, kGu, kDn, UPS, DNK, false, FD, 1, true>(a, grid, s);
-      if (a.B == 8) return launch_fused_t<F, kGu, kDn, UPS, DNK, false, FD, 8, true>(a, grid, s);
+      if (a.B == 1) return launch_fused_t<F, kGu, kDn, UPS, DNK, NORM, FD, 1, true>(a, grid, s);
+      if constexpr (!NORM)
+        if (a.B == 8) return launch_fused_t<F, kGu, kDn, UPS, DNK, false, FD, 8, true>(a, grid, s);
     }
   }
   if constexpr (DNK > 0) {
