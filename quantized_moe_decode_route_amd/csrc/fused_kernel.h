@@ -324,11 +324,11 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   uint64_t ctr_off = a.L.counters, lg_off = a.L.logit_tags, trace_i = (uint64_t)a.trace;
   int G = gridDim.x, NX = a.nx, E = a.E, D = a.D, Bv = a.B, k = a.k;
   asm volatile("" : "+s"(router_i), "+s"(x_i), "+s"(h_i), "+s"(ws_i), "+s"(ctr_off), "+s"(lg_off), "+s"(trace_i));
-  // Full-shape builds take the shape as constants: the vector-path builds
-  // from the first instruction, the matrix-core builds from gate/up on (their
-  // routing measured 1.3 us slower at one token with the constants in it,
-  // their later phases faster).
-  constexpr bool kConstAll = FULL && DNK == 0, kConstLate = FULL && DNK > 0;
+  // Full-shape builds take the shape as constants: from the first
+  // instruction, except the eight-token matrix-core build, which measured
+  // faster with run-time values through the routing and constants from
+  // gate/up on.
+  constexpr bool kConstAll = FULL && (DNK == 0 || CB == 1), kConstLate = FULL && !kConstAll;
   if constexpr (kConstAll) {
     G = kFullG;
     NX = kFullNX;
@@ -350,6 +350,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // row and of the activations (x, or h for the in-kernel norm), issued
   // unconditionally (clamped to a valid row and chunk) before the call's
   // epoch and the XCD counter are requested.
+  // At the full shape d_model is 8 x the block size, so every thread has a
+  // chunk of its own.  (Left to a run-time test, the compiler keeps a path on
+  // which a thread skips its chunk; at the join after the first router dot it
+  // must then wait for that path's loads, and on the real path the wait
+  // covers the arrival atomic's return.)
+  const bool own_chunk = (FULL && kFullD == 8 * kW * kWave) || 8 * (int)threadIdx.x < D;
   const int c8 = min(8 * (int)threadIdx.x, D - 8);
   float4 fha, fhb;       // the in-kernel norm: h chunk (requested before the router row)
   if constexpr (NORM) {
@@ -490,7 +496,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     // LDS for gate/up (F::stage8).
     // The loads are issued unconditionally (clamped to valid rows), h first:
     // the norm then waits for h alone while the router row is in flight.
-    const bool mine = 8 * (int)threadIdx.x < D;  // then c8 = 8 * threadIdx.x
+    const bool mine = own_chunk;  // then c8 = 8 * threadIdx.x
     float4 ha = fha, hb = fhb, w0 = fw0, w1 = fw1;
     if (!mine) ha = hb = make_float4(0.f, 0.f, 0.f, 0.f);
     const double ss = wave_sum_dpp_f64(rms_squares8(ha, hb, 0.0));
@@ -542,13 +548,13 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       // fits (d_model <= 4096): no loop header for the compiler to wait at.
       if (D <= 8 * kW * kWave) {
         if (e == g) {  // the chunk requested first
-          if (8 * (int)threadIdx.x < D) {
+          if (own_chunk) {
             dot8(acc, fw0, fw1, fx);
             take_arrival_after(acc);
 #pragma unroll
             for (int t = 0; t < kMaxTok; ++t) xkeep[t] = fx[t];
           }
-        } else if (8 * (int)threadIdx.x < D) {
+        } else if (own_chunk) {
           chunk(8 * threadIdx.x);
         }
       } else {
@@ -556,7 +562,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
       }
       publish_logits(e, acc);
     }
-    if (early_x && 8 * (int)threadIdx.x < D) {  // after the logits are out: not on their path
+    if (early_x && own_chunk) {  // after the logits are out: not on their path
 #pragma unroll
       for (int t = 0; t < kMaxTok; ++t)
         if (t < B) F::stage8(xkeep[t], threadIdx.x, reinterpret_cast<uint4*>(s_buf) + (size_t)t * kCh * UG, UG);
