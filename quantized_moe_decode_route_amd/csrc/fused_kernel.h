@@ -25,9 +25,11 @@
 //     Gate and up may be in another format than down (template F vs FD).
 //  3. Down.  XCD x requests its first experts' down blocks, gathers its own h
 //     slice, multiplies every down row's slice-x columns by it (partial sums
-//     over d_ff), combines the k ranks of each token in rank order, and
-//     publishes the partial outputs device-wide; the output rows are then
-//     finished by summing the NX partials in XCD order.
+//     over d_ff) and publishes the partial outputs device-wide; the output
+//     rows are then finished by summing the NX partials in XCD order.  The
+//     gate weights enter there: on the matrix-core path they are folded into
+//     h, so a token's experts accumulate in its MFMA accumulators (experts
+//     ascending); the vector path combines the k ranks in rank order.
 //
 // A token's arithmetic does not depend on the other tokens in the call (same
 // lane mapping, same reduction trees), so B=8 rows equal B=1 results bit for
@@ -274,7 +276,7 @@ struct Rings {  // per format, so a format with more live registers can use shal
 };
 template <>
 struct Rings<MxFmt> {  // three gate/up items in flight per wave: at the end of gate/up the last items
-                       // are spread over more waves (a 4-slot ring was 0.9 us slower at B=1)
+                       // are spread over more waves (a 4-slot ring was 0.5 us slower at B=1, 1.2 us at B=8)
   static constexpr int kGU = 3;
   static constexpr int kDN = 7;
 };
@@ -1225,7 +1227,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
   };
   // Gate/up work items are (expert group, row) pairs of this workgroup's
-  // rows, in group-table order (experts ascending; at B=1 in rank order),
+  // rows, in group-table order (experts ascending),
   // handed out by an LDS counter: a wave takes its
   // next item when it requests the item's weights (kRingGU - 1 items ahead),
   // so waves that get their data sooner take more items and all finish
