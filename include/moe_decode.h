@@ -280,8 +280,11 @@ int moe_layer_decode_profiled(const moe_layer_desc* L, const uint16_t* x_bf16, i
  * gathered, down done, partial outputs published, end; slot 11 the clock
  * when the h gather starts and slot 12 when its reads are complete; slot 13
  * the re-read passes thread 0 needed in the logit wait (bits 0..15) and in
- * the h waits (bits 16..31); slot 14 is the workgroup's XCD and slot 15 the
- * raw value of its XCD arrival counter. */
+ * the h waits (bits 16..31); slot 14 is the workgroup's XCD and slot 15 how
+ * it found its index inside the XCD: bit 63 set and the index in the low
+ * bits when it came from the block index (the placement probe saw workgroup
+ * b on XCD b % XCDs), else the raw value of the XCD's arrival counter
+ * (MOE_XCD_INDEX_ATOMIC set in the environment forces the counter). */
 #define MOE_TRACE_FIELDS 16 /* uint64 per workgroup in moe_layer_decode_traced */
 int moe_layer_decode_traced(const moe_layer_desc* L, const uint16_t* x_bf16, int B, float* y, void* ws,
                             size_t ws_bytes, uint64_t* trace, int* trace_blocks, void* stream);

@@ -2,6 +2,8 @@
 // and the dispatch to the per-format kernels (fused_kernel.h).
 #include "fused_kernel.h"
 
+#include <cstdlib>
+
 namespace moe {
 using fused::FusedArgs;
 using fused::kW;
@@ -18,6 +20,12 @@ __global__ __launch_bounds__(kW * kWave, 1) void xcc_map_kernel(uint32_t* out) {
     lds_footprint[0] = xcc_id();
     out[blockIdx.x] = lds_footprint[0];
   }
+}
+
+// Per device: 1 when the probe saw workgroup b on XCD b % nx.
+int& rr_slot(int dev) {
+  static int rr[64] = {0};
+  return rr[dev];
 }
 
 }  // namespace
@@ -106,6 +114,13 @@ int probe_xcd_count(uint32_t* scratch, int grid, hipStream_t s) {
   // Every XCD must hold the same number of workgroups.
   for (int x = 0; x < n; ++x)
     if (count[x] * n != grid) return nx = -1;
+  // Workgroup indices inside an XCD from the block index when the placement
+  // is round-robin (workgroup b on XCD b % n), unless MOE_XCD_INDEX_ATOMIC is
+  // set; otherwise the kernel takes them from an L2 atomic counter.
+  bool rr = true;
+  for (int b = 0; b < grid; ++b) rr = rr && (int)host[b] == b % n;
+  const char* env = std::getenv("MOE_XCD_INDEX_ATOMIC");
+  rr_slot(dev) = rr && !(env && env[0] && env[0] != '0');
   return nx = n;
 }
 
@@ -139,6 +154,10 @@ hipError_t launch_fused_layer(int fmt, int dfmt, const float* router_w, const ui
   a.k = k;
   a.B = B;
   a.nx = xcd_count();
+  {
+    int dev = 0;
+    a.rr_mode = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 ? rr_slot(dev) : 0;
+  }
   const int grid = fused_grid_size();
   const FusedShape sh = fused_shape(fmt, dfmt, B, k, D, Fd, grid, a.nx, down.layout);
   if (!sh.ok) return hipErrorInvalidValue;

@@ -209,6 +209,11 @@ struct FusedArgs {
   uint64_t* trace;
   int E, D, Fd, k, B;
   int nx;  // XCDs (the grid holds grid/nx workgroups on each)
+  // Set when the placement probe saw workgroup b run on XCD b % nx: then a
+  // workgroup's index inside its XCD is blockIdx.x / nx (a workgroup placed
+  // otherwise reports a failed wait).  Otherwise the index comes from an L2
+  // atomic counter.
+  int rr_mode;
 };
 
 __device__ __forceinline__ uint32_t xcc_id() {
@@ -325,7 +330,9 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   uint64_t router_i = (uint64_t)a.router_w, x_i = (uint64_t)a.x, h_i = (uint64_t)a.hn, ws_i = (uint64_t)a.ws;
   uint64_t ctr_off = a.L.counters, lg_off = a.L.logit_tags, trace_i = (uint64_t)a.trace;
   int G = gridDim.x, NX = a.nx, E = a.E, D = a.D, Bv = a.B, k = a.k;
-  asm volatile("" : "+s"(router_i), "+s"(x_i), "+s"(h_i), "+s"(ws_i), "+s"(ctr_off), "+s"(lg_off), "+s"(trace_i));
+  int rr_mode = a.rr_mode;
+  asm volatile("" : "+s"(router_i), "+s"(x_i), "+s"(h_i), "+s"(ws_i), "+s"(ctr_off), "+s"(lg_off), "+s"(trace_i),
+               "+s"(rr_mode));
   // Full-shape builds take the shape as constants: from the first
   // instruction, except the eight-token matrix-core build, which measured
   // faster with run-time values through the routing and constants from
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
   // partial sums (an empty asm reading them).
   bool arrival_pending = true;
   auto take_arrival = [&]() {
-    if (arrival_pending && threadIdx.x == 0)
+    if (arrival_pending && threadIdx.x == 0 && !rr_mode)
       xcd_arrival = __hip_atomic_fetch_add(ctr + kCtrXcdBase + xcd, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     arrival_pending = false;
   };
@@ -741,10 +748,15 @@ __global__ __launch_bounds__(kW * kWave, 1) void fused_layer_kernel(FusedArgs a)
     }
   }
   if (threadIdx.x == 0) {  // the arrival counter has long returned by now
-    s_jx = (int)(xcd_arrival % (uint32_t)GX);
+    if (rr_mode) {
+      if (xcd != g % NX) s_timeout = 1;  // not the placement the probe saw: reported as a failed wait
+      s_jx = (g / NX) % GX;
+    } else {
+      s_jx = (int)(xcd_arrival % (uint32_t)GX);
+    }
     if (traced) {
       s_trace[kTracePoints - 2] = (uint64_t)xcd;
-      s_trace[kTracePoints - 1] = (uint64_t)xcd_arrival;
+      s_trace[kTracePoints - 1] = rr_mode ? (1ull << 63) | (uint64_t)(g / NX) : (uint64_t)xcd_arrival;
     }
   }
   // Stage the activations requested above (their loads have long returned:
