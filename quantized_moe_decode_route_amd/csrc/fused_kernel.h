@@ -7,10 +7,12 @@
 // the data it consumes.  All exchanges use agent-coherent 64-bit accesses
 // (workgroup-scope stores are not reliably seen by other compute units of the
 // same XCD while the kernel runs).  A workgroup learns its XCD from the
-// XCC_ID hardware register and its index inside the XCD from an L2-local
-// counter: with one workgroup per compute unit (the LDS footprint allows no
-// more), every XCD holds exactly grid/NX of them, whatever order the
-// dispatcher used.
+// XCC_ID hardware register.  Its index inside the XCD is blockIdx / NX when
+// the host's placement probe saw the round-robin placement (workgroup b on
+// XCD b % NX; a workgroup placed otherwise reports a failed wait), else it
+// comes from an L2-local counter: with one workgroup per compute unit (the
+// LDS footprint allows no more), every XCD holds exactly grid/NX of them,
+// whatever order the dispatcher used.
 //
 //  1. Routing.  Workgroup g computes expert g's router logits for every token
 //     (fp64) and publishes them device-wide; in a layer stack at B=1 it first
