@@ -29,23 +29,40 @@ HIP_FLAGS = [
 FUSED_FLAGS = ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
-def _compile(src: str) -> str:
+# fused_units.hip holds the layer kernel's instantiations in this many units,
+# compiled separately (-DMOE_FUSED_UNIT=i) so they build in parallel.
+FUSED_UNITS = 5
+
+
+def _compile(job: tuple[str, int | None]) -> str:
+    src, unit = job
     os.makedirs(BUILD_DIR, exist_ok=True)
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    name = os.path.basename(src) + ("" if unit is None else f".{unit}")
+    obj = os.path.join(BUILD_DIR, name + ".o")
     extra = FUSED_FLAGS if os.path.basename(src).startswith("fused") else []
+    if unit is not None:
+        extra = [*extra, f"-DMOE_FUSED_UNIT={unit}"]
     cmd = [HIPCC, *HIP_FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {name}:\n{r.stderr}")
     return obj
 
 
 def build(jobs: int | None = None) -> str:
     """Compile every source under csrc/ and link libmoedecode.so (always rebuilds)."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    jobs = jobs or min(8, len(srcs))
+    work = []
+    for src in srcs:
+        if os.path.basename(src) == "fused_units.hip":
+            work += [(src, i) for i in range(FUSED_UNITS)]
+        else:
+            work.append((src, None))
+    # the slow units first, so the pool does not end on one of them
+    work.sort(key=lambda j: (j[1] is None, j))
+    jobs = jobs or min(8, len(work))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(_compile, work))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

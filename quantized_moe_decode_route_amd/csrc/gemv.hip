@@ -106,6 +106,61 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ w
   }
 }
 
+constexpr int kGemvXs = 16384;  // fp32 activations staged per chunk of tokens
+constexpr int kGemvThreads = 256;  // the stand-alone matvec's workgroup size
+
+// The dots of a wave's kGemvR register-held rows with TT consecutive staged
+// tokens (slots s0.. of the chunk, tokens t.. of the call), stored to y.  The
+// TT tokens' accumulations are independent chains, so they overlap; each
+// token still adds its units in ascending order and then sums over the wave,
+// so its result has the same bits whatever TT is.  A unit's decode does not
+// depend on the activations and is shared by the TT tokens.
+template <class F, int UPL, int TT>
+__device__ __forceinline__ void regs_tokens(const typename F::Raw (&raw)[kGemvR][UPL], const float* xs, int K, int s0,
+                                            int t, int N, int row0, float* __restrict__ y) {
+  constexpr int C = F::kUnitW / 4;
+  const int U = F::units(K), lane = lane_id();
+  float acc[TT][kGemvR];
+#pragma unroll
+  for (int j = 0; j < TT; ++j)
+#pragma unroll
+    for (int r = 0; r < kGemvR; ++r) acc[j][r] = 0.0f;
+#pragma unroll
+  for (int i = 0; i < UPL; ++i) {
+    const int u = lane + kWave * i;
+    if (u < U) {
+      float xv[TT][F::kUnitW];
+#pragma unroll
+      for (int j = 0; j < TT; ++j) {
+        const float4* xt4 = reinterpret_cast<const float4*>(xs) + (s0 + j) * (K / 4) + u;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const float4 v = xt4[c * U];
+          xv[j][4 * c] = v.x;
+          xv[j][4 * c + 1] = v.y;
+          xv[j][4 * c + 2] = v.z;
+          xv[j][4 * c + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kGemvR; ++r)
+#pragma unroll
+        for (int j = 0; j < TT; ++j) acc[j][r] += F::dot(raw[r][i], (uint32_t)u & 3u, xv[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TT; ++j)
+#pragma unroll
+    for (int r = 0; r < kGemvR; ++r) acc[j][r] = wave_sum(acc[j][r]);
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < TT; ++j)
+#pragma unroll
+      for (int r = 0; r < kGemvR; ++r)
+        if (row0 + r < N) y[(int64_t)(t + j) * N + row0 + r] = acc[j][r];
+  }
+}
+
 // The same matvec with the wave's weights held in registers: every lane
 // first requests all of its units of the kGemvR rows (UPL units per row, one
 // memory round trip), then each token's dots run from those registers, so
@@ -113,11 +168,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ w
 // activations of as many tokens as fit in LDS (64 KB) at a time, so a
 // token's dots wait for LDS rather than for one L2 round trip per token.
 // The per-token arithmetic is rows_dot's (a lane adds its units in ascending
-// order, then the wave sums), so the results are the same bits.
-constexpr int kGemvXs = 16384;  // fp32 activations staged per chunk of tokens
-
+// order, then the wave sums), so the results are the same bits; staged
+// tokens are taken up to four at a time (regs_tokens), which keeps up to
+// eight independent accumulations in flight on the one wave of each SIMD.
 template <class F, int UPL>
-__global__ __launch_bounds__(256) void gemv_regs_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ sc,
+__global__ __launch_bounds__(kGemvThreads) void gemv_regs_kernel(const uint8_t* __restrict__ w, const uint16_t* __restrict__ sc,
                                                         int N, int K, const float* __restrict__ x, int B,
                                                         float* __restrict__ y) {
   __shared__ __align__(16) float xs[kGemvXs];
@@ -126,6 +181,9 @@ __global__ __launch_bounds__(256) void gemv_regs_kernel(const uint8_t* __restric
   const bool rows_here = row0 < N;  // waves without rows still stage activations
   const int U = F::units(K);
   const int lane = lane_id();
+  // tokens per group: as many as the registers hold without spilling (the
+  // staged activations of a group take TT * kUnitW registers)
+  constexpr int kTok = F::kUnitW >= 64 ? (UPL >= 2 ? 1 : 2) : 4;
   typename F::Raw raw[kGemvR][UPL];
 #pragma unroll
   for (int r = 0; r < kGemvR; ++r) {
@@ -153,7 +211,16 @@ __global__ __launch_bounds__(256) void gemv_regs_kernel(const uint8_t* __restric
       __syncthreads();
     }
     if (!rows_here) continue;
-    for (int t = t0; t < t0 + nt; ++t) {
+    int t = t0;
+    if (tc > 0) {  // staged tokens: kTok (then fewer) at a time
+      if constexpr (kTok >= 4)
+        for (; t + 4 <= t0 + nt; t += 4) regs_tokens<F, UPL, 4>(raw, xs, K, t - t0, t, N, row0, y);
+      if constexpr (kTok >= 2)
+        for (; t + 2 <= t0 + nt; t += 2) regs_tokens<F, UPL, 2>(raw, xs, K, t - t0, t, N, row0, y);
+      for (; t < t0 + nt; ++t) regs_tokens<F, UPL, 1>(raw, xs, K, t - t0, t, N, row0, y);
+      continue;
+    }
+    for (; t < t0 + nt; ++t) {
       float acc[kGemvR];
 #pragma unroll
       for (int r = 0; r < kGemvR; ++r) acc[r] = 0.0f;
@@ -161,25 +228,9 @@ __global__ __launch_bounds__(256) void gemv_regs_kernel(const uint8_t* __restric
       for (int i = 0; i < UPL; ++i) {
         const int u = lane + kWave * i;
         if (u < U) {
-          if (tc > 0) {
-            constexpr int C = F::kUnitW / 4;
-            const float4* xt4 = reinterpret_cast<const float4*>(xs) + (t - t0) * (K / 4) + u;
-            float xv[F::kUnitW];
+          const float* xt = x + (int64_t)t * K + (int64_t)F::kUnitW * u;
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-              const float4 v = xt4[c * U];
-              xv[4 * c] = v.x;
-              xv[4 * c + 1] = v.y;
-              xv[4 * c + 2] = v.z;
-              xv[4 * c + 3] = v.w;
-            }
-#pragma unroll
-            for (int r = 0; r < kGemvR; ++r) acc[r] += F::dot(raw[r][i], (uint32_t)u & 3u, xv);
-          } else {
-            const float* xt = x + (int64_t)t * K + (int64_t)F::kUnitW * u;
-#pragma unroll
-            for (int r = 0; r < kGemvR; ++r) acc[r] += F::dot(raw[r][i], (uint32_t)u & 3u, xt);
-          }
+          for (int r = 0; r < kGemvR; ++r) acc[r] += F::dot(raw[r][i], (uint32_t)u & 3u, xt);
         }
       }
 #pragma unroll
@@ -200,11 +251,11 @@ hipError_t launch_gemv_f(const uint8_t* w, const uint16_t* scale, int N, int K, 
   const dim3 grid((N + rows_per_block - 1) / rows_per_block);
   const int upl = (K / F::kUnitW + kWave - 1) / kWave;  // units per lane and row
   if (upl <= 1)
-    hipLaunchKernelGGL((gemv_regs_kernel<F, 1>), grid, dim3(256), 0, s, w, scale, N, K, x, B, y);
+    hipLaunchKernelGGL((gemv_regs_kernel<F, 1>), grid, dim3(kGemvThreads), 0, s, w, scale, N, K, x, B, y);
   else if (upl <= 2)
-    hipLaunchKernelGGL((gemv_regs_kernel<F, 2>), grid, dim3(256), 0, s, w, scale, N, K, x, B, y);
+    hipLaunchKernelGGL((gemv_regs_kernel<F, 2>), grid, dim3(kGemvThreads), 0, s, w, scale, N, K, x, B, y);
   else if (upl <= 4)
-    hipLaunchKernelGGL((gemv_regs_kernel<F, 4>), grid, dim3(256), 0, s, w, scale, N, K, x, B, y);
+    hipLaunchKernelGGL((gemv_regs_kernel<F, 4>), grid, dim3(kGemvThreads), 0, s, w, scale, N, K, x, B, y);
   else  // long rows: stream them per token
     hipLaunchKernelGGL(gemv_kernel<F>, grid, dim3(256), 0, s, w, scale, N, K, x, B, y);
   return hipGetLastError();
