@@ -17,7 +17,8 @@ namespace {
 // acc[r] = dot of row r with one token's activation x, over the whole row.
 // Tokens that share rows call this once each; the repeated reads of the same
 // rows by the same wave are served by the caches (the stand-alone matvec
-// keeps short rows in registers instead: gemv_regs_kernel).
+// keeps short rows in registers instead, gemv_regs_kernel, and passes over
+// long rows once per four tokens, rows_dot_tokens).
 template <class F, int R>
 __device__ __forceinline__ void rows_dot(const typename F::Row (&rows)[R], int K, const float* __restrict__ x,
                                          float (&acc)[R]) {
@@ -33,6 +34,33 @@ __device__ __forceinline__ void rows_dot(const typename F::Row (&rows)[R], int K
   }
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = wave_sum(acc[r]);
+}
+
+// rows_dot for TT tokens at once (token j's activation at x + j * K): each
+// unit of the rows is loaded once for the TT tokens, and every token's sum
+// is taken in rows_dot's order, so its bits are rows_dot's.
+template <class F, int R, int TT>
+__device__ __forceinline__ void rows_dot_tokens(const typename F::Row (&rows)[R], int K,
+                                                const float* __restrict__ x, float (&acc)[TT][R]) {
+  const int U = F::units(K);
+#pragma unroll
+  for (int j = 0; j < TT; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[j][r] = 0.0f;
+  for (int u = lane_id(); u < U; u += kWave) {
+    typename F::Raw raw[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) F::load(rows[r], u, raw[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int j = 0; j < TT; ++j)
+        acc[j][r] += F::dot(raw[r], (uint32_t)u & 3u, x + (int64_t)j * K + (int64_t)F::kUnitW * u);
+  }
+#pragma unroll
+  for (int j = 0; j < TT; ++j)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[j][r] = wave_sum(acc[j][r]);
 }
 
 // Same for rows n[r] of a matrix [N][K] stored in MOE_LAYOUT_TILE256: unit u
@@ -95,7 +123,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ w
   typename F::Row rows[kGemvR];
 #pragma unroll
   for (int r = 0; r < kGemvR; ++r) rows[r] = F::row(w, sc, min(row0 + r, N - 1), K);
-  for (int t = 0; t < B; ++t) {
+  int t = 0;
+  for (; t + 4 <= B; t += 4) {  // four tokens per pass over the rows
+    float acc[4][kGemvR];
+    rows_dot_tokens<F, kGemvR, 4>(rows, K, x + (int64_t)t * K, acc);
+    if (lane_id() == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < kGemvR; ++r)
+          if (row0 + r < N) y[(int64_t)(t + j) * N + row0 + r] = acc[j][r];
+    }
+  }
+  for (; t < B; ++t) {
     float acc[kGemvR];
     rows_dot<F, kGemvR>(rows, K, x + (int64_t)t * K, acc);
     if (lane_id() == 0) {

@@ -89,6 +89,29 @@ def test_gemv_every_token_count_and_width_invariance():
         assert np.array_equal(yb, y1[:B]), f"width drift at B={B}"
 
 
+@pytest.mark.parametrize("fmt,k", [("mxfp4", 8192 + 32), ("int4g32", 16384), ("q2k", 16384 + 256)])
+def test_gemv_long_rows(fmt, k):
+    """Rows of more than 256 units (more than the register-held path keeps per
+    lane) are streamed, four tokens per pass: parity at every token count that
+    mixes four-token passes with single tokens, and each token's result
+    bitwise the same whatever B is."""
+    n = 21  # three workgroups of 8 rows, the last one ragged
+    if fmt == "mxfp4":
+        w = _mx(700, n, k)
+    elif fmt == "q2k":
+        w = _q2(701, n, k)
+    else:
+        w = synth.int4_raw(synth.tensor_key(702, synth.TAG_INT4, 0, 0, 0), n, k)
+    x = synth.token_f32(703, 8, k)
+    ref = oracle.gemv(fmt, w, n, k, x.astype(np.float64))
+    y8 = _run(fmt, w, n, k, x)
+    assert_parity(y8, ref, what=f"{fmt} {n}x{k} B=8")
+    for B in (1, 3, 4, 5):
+        yb = _run(fmt, w, n, k, x[:B])
+        assert_parity(yb, ref[:B], what=f"{fmt} {n}x{k} B={B}")
+        assert np.array_equal(yb, y8[:B]), f"{fmt}: width drift at B={B}"
+
+
 def test_gemv_exact_integer_case():
     # e = 127 and codes {0,2,4,5,6,7} give small integers; with integer x the
     # fp32 sums are exact, so the GPU must equal the oracle exactly.
