@@ -152,8 +152,8 @@ constexpr int kGemvThreads = 256;  // the stand-alone matvec's workgroup size
 // The dots of a wave's kGemvR register-held rows with TT consecutive staged
 // tokens (slots s0.. of the chunk, tokens t.. of the call), stored to y.  The
 // TT tokens' accumulations are independent chains, so they overlap; each
-// token still adds its units in ascending order and then sums over the wave,
-// so its result has the same bits whatever TT is.  A unit's decode does not
+// token still adds its units in ascending order and then sums over the wave
+// (one fixed DPP tree), so its result has the same bits whatever TT is.  A unit's decode does not
 // depend on the activations and is shared by the TT tokens.
 template <class F, int UPL, int TT>
 __device__ __forceinline__ void regs_tokens(const typename F::Raw (&raw)[kGemvR][UPL], const float* xs, int K, int s0,
@@ -191,8 +191,8 @@ __device__ __forceinline__ void regs_tokens(const typename F::Raw (&raw)[kGemvR]
 #pragma unroll
   for (int j = 0; j < TT; ++j)
 #pragma unroll
-    for (int r = 0; r < kGemvR; ++r) acc[j][r] = wave_sum(acc[j][r]);
-  if (lane == 0) {
+    for (int r = 0; r < kGemvR; ++r) acc[j][r] = wave_sum_dpp_f32(acc[j][r]);
+  if (lane == kWave - 1) {  // where the DPP tree leaves the sums
 #pragma unroll
     for (int j = 0; j < TT; ++j)
 #pragma unroll
@@ -207,8 +207,8 @@ __device__ __forceinline__ void regs_tokens(const typename F::Raw (&raw)[kGemvR]
 // the weights are loaded once whatever B is.  The workgroup stages the
 // activations of as many tokens as fit in LDS (64 KB) at a time, so a
 // token's dots wait for LDS rather than for one L2 round trip per token.
-// The per-token arithmetic is rows_dot's (a lane adds its units in ascending
-// order, then the wave sums), so the results are the same bits; staged
+// Per token a lane adds its units in ascending order, then the wave sums in
+// a fixed DPP tree, so a token's result does not depend on B; staged
 // tokens are taken up to four at a time (regs_tokens), which keeps up to
 // eight independent accumulations in flight on the one wave of each SIMD.
 template <class F, int UPL>
@@ -274,8 +274,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_regs_kernel(const uint8_t* 
         }
       }
 #pragma unroll
-      for (int r = 0; r < kGemvR; ++r) acc[r] = wave_sum(acc[r]);
-      if (lane == 0) {
+      for (int r = 0; r < kGemvR; ++r) acc[r] = wave_sum_dpp_f32(acc[r]);
+      if (lane == kWave - 1) {
 #pragma unroll
         for (int r = 0; r < kGemvR; ++r)
           if (row0 + r < N) y[(int64_t)t * N + row0 + r] = acc[r];
