@@ -83,22 +83,7 @@ __device__ __forceinline__ uint64_t ld_xcd(const uint64_t* p) {
 }
 // ---------------------------------------------------------------- DPP reductions
 
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
-                                                               false));
-}
-
-// Sum over the wave in a fixed tree; the total lands in lane 63.
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v += dpp_f<0xB1>(v);        // quad_perm [1,0,3,2]
-  v += dpp_f<0x4E>(v);        // quad_perm [2,3,0,1]
-  v += dpp_f<0x141>(v);       // row_half_mirror
-  v += dpp_f<0x140>(v);       // row_mirror
-  v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
-  v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
-  return v;
-}
+// (dpp_f and the wave sum wave_sum_dpp are in moe_internal.h.)
 
 // Sum over aligned groups of G lanes (G = 1, 2, 4, 8 or 16); every lane of a
 // group ends with the group's sum.

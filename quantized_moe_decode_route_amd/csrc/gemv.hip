@@ -191,7 +191,7 @@ __device__ __forceinline__ void regs_tokens(const typename F::Raw (&raw)[kGemvR]
 #pragma unroll
   for (int j = 0; j < TT; ++j)
 #pragma unroll
-    for (int r = 0; r < kGemvR; ++r) acc[j][r] = wave_sum_dpp_f32(acc[j][r]);
+    for (int r = 0; r < kGemvR; ++r) acc[j][r] = wave_sum_dpp(acc[j][r]);
   if (lane == kWave - 1) {  // where the DPP tree leaves the sums
 #pragma unroll
     for (int j = 0; j < TT; ++j)
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_regs_kernel(const uint8_t* 
         }
       }
 #pragma unroll
-      for (int r = 0; r < kGemvR; ++r) acc[r] = wave_sum_dpp_f32(acc[r]);
+      for (int r = 0; r < kGemvR; ++r) acc[r] = wave_sum_dpp(acc[r]);
       if (lane == kWave - 1) {
 #pragma unroll
         for (int r = 0; r < kGemvR; ++r)

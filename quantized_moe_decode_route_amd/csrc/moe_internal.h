@@ -124,15 +124,21 @@ __device__ __forceinline__ double dpp_d(double v) {
   const int hi = dpp_i<CTRL, ROW_MASK>(__double2hiint(v), 0);
   return __hiloint2double(hi, lo);
 }
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                                               false));
+}
+
 // Sum over the wave in a fixed DPP tree, without LDS round trips; the total
 // lands in lane 63.
-__device__ __forceinline__ float wave_sum_dpp_f32(float v) {
-  v += __int_as_float(dpp_i<0xB1>(__float_as_int(v), 0));        // quad_perm [1,0,3,2]
-  v += __int_as_float(dpp_i<0x4E>(__float_as_int(v), 0));        // quad_perm [2,3,0,1]
-  v += __int_as_float(dpp_i<0x141>(__float_as_int(v), 0));       // row_half_mirror
-  v += __int_as_float(dpp_i<0x140>(__float_as_int(v), 0));       // row_mirror
-  v += __int_as_float(dpp_i<0x142, 0xA>(__float_as_int(v), 0));  // row_bcast:15 into rows 1, 3
-  v += __int_as_float(dpp_i<0x143, 0xC>(__float_as_int(v), 0));  // row_bcast:31 into rows 2, 3
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<0xB1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);        // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);       // row_half_mirror
+  v += dpp_f<0x140>(v);       // row_mirror
+  v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
