@@ -99,7 +99,11 @@ int moe_device_check(void);
 /* ------------------------------------------------------------------ matvec
  * y[b][n] = sum_k W[n][k] * x[b][k] for b < B, with the weights decoded
  * inside the kernel and fp32 accumulation.  x fp32 [B][K], y fp32 [B][N]
- * (overwritten).  1 <= B <= MOE_MAX_TOKENS; every token reuses one read of W.
+ * (overwritten).  1 <= B <= MOE_MAX_TOKENS.  W is read from memory once per
+ * call for rows of up to 8192 weights (16384 for Q2_K), held in registers
+ * across the B tokens; longer rows are streamed once per four tokens, the
+ * later passes served by the caches.  A token's y does not depend on B (bit
+ * for bit).
  * Alignment: MXFP4 and Q2_K blocks 4-byte aligned, INT4 codes 16-byte
  * aligned, x 16-byte aligned.
  * Source: the per-block decode of the formats above; the matvec against the
